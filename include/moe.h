@@ -1,0 +1,234 @@
+/*
+ * moe.h — C ABI of the batch-invariant MoE layer forward pass for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The layer: router scoring + top-k (or fixed hash routing), dispatch
+ * (token permutation by expert), a grouped SwiGLU expert FFN over the routed
+ * (token, expert) rows plus one always-on shared expert, and a weighted
+ * combine.  Sources (web pages, cited by title and section):
+ *   [DS] "6 基建与训练稳定性优化" — DeepSeek-V4 infrastructure walkthrough
+ *        (liyongzhi.xyz, deepseek_v4 sections/06-infra): 6.1 dispatch ->
+ *        compute -> combine; 6.2 FP4 (E2M1) expert weights with block scales;
+ *        6.3 learned routing (scores = W h, top-k) and hash routing
+ *        (expert = hash(token id) mod E); 6.5 SwiGLU = SiLU(W_g x) * (W_v x).
+ *   [FW] "MoE 模型中的訓練與推論一致性：數值漂移發生之處" — Fireworks AI post
+ *        on MoE train/inference parity: floating-point addition is not
+ *        associative; the MoE finalize is a per-token weighted sum of the
+ *        top-k expert outputs, followed by += shared expert (trap 3); keep the
+ *        k contributions in fp32 and cast once (Qwen3.5-MoE case study);
+ *        per-fusion control flags (lessons).
+ *   [MT] "美团把训练和推理的概率做到逐位相同:分歧藏在一个加法顺序里" — bitwise
+ *        parity needs every GEMM to see its full K (no split sums).
+ *   [LD] feedbbs.com/linuxdo/72580 — shared experts see every token and are
+ *        added to the weighted routed sum (section 共享专家); GLU gate/up
+ *        branches (section on GLU); token dropping makes outputs depend on the
+ *        batch (section on output determinism) — this library never drops.
+ *   [V4] nxmr.cn/news/146660 section 2.2 — the router is a small linear layer
+ *        producing E logits, softmax weights, top-k.
+ *
+ * Determinism contract: for fixed inputs every output row is bitwise
+ * identical for any batch size T, any batch composition or order, any stream
+ * and any repeat.  Routing keys use a fixed fp32 accumulation order and a
+ * library-defined exp (below); the expert GEMMs use one MFMA instruction shape
+ * and one K order for every T, K is never split across workgroups, and no
+ * floating-point atomics are used anywhere.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers owned by the caller (plain device memory,
+ *     16-byte aligned).  The library never allocates or frees memory and keeps
+ *     no state except a thread-local error message.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every
+ *     call only enqueues kernels on that stream: no host synchronisation and
+ *     no host<->device copies.
+ *   - All arguments are validated on the host before anything is enqueued.  On
+ *     error nothing is launched, outputs are untouched, and a negative
+ *     moe_status is returned; moe_last_error() describes it.  Launch failures
+ *     map to MOE_ERR_HIP.  No C++ exception crosses the ABI.
+ *   - Activations/outputs are row-major [rows, cols]; weights are [out, in]
+ *     with the reduction dimension contiguous (as nn.Linear).
+ *   - Unchecked preconditions: inputs are finite (non-finite values give
+ *     unspecified but deterministic results); E8M0 scale bytes are <= 252
+ *     (dequantised values stay finite in bf16); topk_idx values handed to
+ *     moe_permute / moe_combine are in [0, E) and distinct per token.
+ *   - Limits: 1 <= k <= 32, k <= E <= 1024, T >= 0 (T = 0 is a no-op),
+ *     D, I, I_shared multiples of 32 and >= 32.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_TOPK 32
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = -1,        /* a required pointer is NULL */
+  MOE_ERR_SHAPE = -2,       /* a size is out of range or inconsistent */
+  MOE_ERR_DTYPE = -3,       /* unsupported dtype combination */
+  MOE_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
+  MOE_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than required */
+  MOE_ERR_UNSUPPORTED = -6, /* valid request this build does not implement */
+  MOE_ERR_HIP = -7          /* a HIP launch failed */
+} moe_status;
+
+/* MOE_MXFP4 is a weight format only: E2M1 codes packed two per byte (element
+ * 2i in the low nibble) [rows, cols/2] plus one E8M0 scale byte per 32
+ * consecutive elements along the reduction axis [rows, cols/32]; value =
+ * e2m1(code) * 2^(scale - 127) (OCP Microscaling v1.0; [DS] 6.2). */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP4 = 2 } moe_dtype;
+
+typedef enum { MOE_ROUTE_SOFTMAX = 0, MOE_ROUTE_SIGMOID = 1, MOE_ROUTE_HASH = 2 } moe_route;
+
+/* Expert weights of G experts (G = E routed, or 1 shared), each row-major:
+ *   gate, up: [G, I, D]   down: [G, D, I]
+ * MOE_MXFP4: gate/up/down hold packed codes ([G, I, D/2], [G, D, I/2]) and
+ * gate_scale/up_scale [G, I, D/32], down_scale [G, D, I/32] hold E8M0 bytes;
+ * the scale pointers must be NULL for other dtypes.
+ * dtype must equal the activation dtype, except that MOE_MXFP4 weights go
+ * with MOE_BF16 activations. */
+typedef struct {
+  const void* gate;
+  const void* up;
+  const void* down;
+  const uint8_t* gate_scale;
+  const uint8_t* up_scale;
+  const uint8_t* down_scale;
+  moe_dtype dtype;
+} moe_expert_weights;
+
+/* ---------------------------------------------------------------------------
+ * moe_router_topk — routing ([DS] 6.3 learned routing and hash routing; [V4]
+ * 2.2 linear router + softmax + top-k).
+ *
+ *  x [T, D] (act = MOE_F32 or MOE_BF16), w_router [E, D] (same dtype),
+ *  bias [E] fp32 or NULL (= 0).  Outputs topk_idx [T, k] int32 in rank order
+ *  and topk_w [T, k] fp32.
+ *
+ *  Logits: L[t,e] = sum_d x[t,d] w[e,d] in fp32 with this fixed order: 64
+ *  partial sums start at +0; element d is added with fmaf to partial
+ *  (d/8) mod 64, d increasing; then partial[j] += partial[j+m] for
+ *  m = 32, 16, 8, 4, 2, 1 (a pairwise tree); L = partial[0].
+ *  exp is this library's routing exp: n = rint(x*fp32(log2 e)),
+ *  r = fma(-n, fp32(ln2), x), r = fma(-n, fp32(ln2 - fp32(ln2)), r),
+ *  p = degree-7 Taylor polynomial with fp32(1/j!) coefficients by Horner with
+ *  fma, result p * 2^n (two exact scalings outside the normal range);
+ *  x > 89 -> +inf, x < -104 -> +0.
+ *   MOE_ROUTE_SOFTMAX: key = L (+ bias); w_j = exp(L_j - L_top) / Z.
+ *   MOE_ROUTE_SIGMOID: s = 1/(1 + exp(-L)) (IEEE division), key = s (+ bias);
+ *                      w_j = s_j / Z.  The bias only decides selection.
+ *   Z sums the selected terms in ascending expert id, in fp32, from +0.
+ *  Selection: the k largest keys, ties to the lower expert id (+0 == -0).
+ *   MOE_ROUTE_HASH: x, w_router, bias unused (may be NULL); token_ids [T]
+ *                   int32 required.  Slot j takes
+ *                   fmix32(tid + j*0x9E3779B9 mod 2^32) mod E (MurmurHash3
+ *                   finaliser), stepping to (c+1) mod E past experts already
+ *                   taken; w = 1/k; topk_idx is in slot order.
+ *  workspace: moe_router_workspace_bytes(T, E) bytes (logits); may be NULL
+ *  when that is 0 (hash routing).
+ * ------------------------------------------------------------------------- */
+size_t moe_router_workspace_bytes(int64_t T, int E, moe_route mode);
+int moe_router_topk(const void* x, moe_dtype act, const void* w_router, const float* bias,
+                    const int32_t* token_ids, int64_t T, int D, int E, int k, moe_route mode,
+                    int32_t* topk_idx, float* topk_w, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* moe_routing_scores — the routing scores of the selection step, element by
+ * element, bit-identical to what moe_router_topk uses: MOE_ROUTE_SIGMOID gives
+ * 1/(1 + exp(-l)), MOE_ROUTE_SOFTMAX gives exp(l) (the routing exp above).
+ * logits, out: [n] fp32.  For callers that log or reuse router probabilities. */
+int moe_routing_scores(const float* logits, int64_t n, moe_route mode, float* out, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_permute — dispatch ([DS] 6.1: tokens go to their experts): the stable
+ * counting sort of the T*k (token, slot) pairs by expert id.
+ *
+ *  expert_counts [E]: rows per expert; expert_offsets [E+1]: exclusive prefix
+ *  sum (expert_offsets[E] = T*k); row_token [T*k]: token of each permuted row
+ *  (rows of one expert in ascending token order); pair_row [T*k]: permuted row
+ *  of pair (t, j), index t*k + j.  No capacity limit, no dropping.
+ *  If x is not NULL, also gathers x_perm[r] = x[row_token[r]] ([T*k, D], act).
+ *  workspace: moe_permute_workspace_bytes(T, E) bytes.
+ * ------------------------------------------------------------------------- */
+size_t moe_permute_workspace_bytes(int64_t T, int E);
+int moe_permute(const int32_t* topk_idx, int64_t T, int k, int E, int32_t* expert_counts,
+                int32_t* expert_offsets, int32_t* row_token, int32_t* pair_row, const void* x,
+                moe_dtype act, int D, void* x_perm, void* workspace, size_t workspace_bytes,
+                void* stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_grouped_swiglu — expert compute ([DS] 6.5 SwiGLU; [LD] GLU branches):
+ * for every row r of expert e (expert_offsets[e] <= r < expert_offsets[e+1]),
+ *   g = W_gate[e] a_r, u = W_up[e] a_r        (fp32 accumulation, full K = D)
+ *   h = round(silu(g) * u),  silu(g) = g / (1 + e^-g)
+ *   out[r] = round(W_down[e] h)               (fp32 accumulation, full K = I)
+ * where a_r = x_rows[row_index[r]] if row_index is not NULL, else x_rows[r],
+ * and round() is bf16 round-to-nearest-even (bf16/MXFP4 weights) or the fp32
+ * value itself (fp32).  MXFP4 weights are decoded exactly to bf16 first, so
+ * their result equals the bf16 path on the decoded weights bit for bit.
+ * Rows of one expert never interact: each row's output is independent of the
+ * other rows and of their number.
+ *  R: number of rows (= expert_offsets[E]); for a shared expert pass E = 1 and
+ *  expert_offsets = {0, T}.  flags: must be 0 (reserved).
+ *  workspace: moe_grouped_swiglu_workspace_bytes(R, I, act) bytes (h).
+ * ------------------------------------------------------------------------- */
+size_t moe_grouped_swiglu_workspace_bytes(int64_t R, int I, moe_dtype act);
+int moe_grouped_swiglu(const void* x_rows, const int32_t* row_index,
+                       const int32_t* expert_offsets, int64_t R, int E, int D, int I,
+                       const moe_expert_weights* w, moe_dtype act, uint32_t flags, void* out,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_combine — the MoE finalize ([FW] trap 3 and case study):
+ *   acc = +0; for each of token t's experts in ascending expert id:
+ *       acc = fmaf(topk_w[t,j], float(expert_out[pair_row[t*k+j]]), acc)
+ *   if shared_out: acc = acc + float(shared_out[t])
+ *   y[t] = round(acc)       (bf16 RNE, or fp32 as is)
+ *  expert_out [T*k, D], shared_out [T, D] or NULL, y [T, D], all act dtype.
+ * ------------------------------------------------------------------------- */
+int moe_combine(const void* expert_out, const int32_t* topk_idx, const float* topk_w,
+                const int32_t* pair_row, const void* shared_out, int64_t T, int k, int D,
+                moe_dtype act, void* y, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_layer_forward — the whole layer: route, permute, grouped SwiGLU over the
+ * routed rows and the shared expert (one launch for both), combine.  y [T, D].
+ * The residual connection is not part of the layer.
+ *  routed: E experts; shared: NULL (no shared expert, I_shared ignored) or one
+ *  expert with inter dim I_shared (bf16 when routed weights are MXFP4).
+ *  flags: must be 0 (reserved for per-fusion variants).
+ *  workspace: moe_layer_workspace_bytes(...) bytes.
+ * ------------------------------------------------------------------------- */
+size_t moe_layer_workspace_bytes(int64_t T, int D, int E, int k, int I, int I_shared,
+                                 moe_dtype act, moe_dtype w);
+int moe_layer_forward(const void* x, const int32_t* token_ids, const void* w_router,
+                      const float* bias, const moe_expert_weights* routed,
+                      const moe_expert_weights* shared, int64_t T, int D, int E, int k, int I,
+                      int I_shared, moe_route mode, moe_dtype act, uint32_t flags, void* y,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Stage timing (measurement only).  When set, the next moe_layer_forward
+ * calls on this host thread record events[0] before the first kernel and
+ * events[i+1] after stage i on the call's stream; stages: 0 routing,
+ * 1 permutation, 2 gate/up SwiGLU GEMM, 3 down GEMM, 4 combine
+ * (MOE_STAGE_EVENTS events).  The events are hipEvent_t handles created by the
+ * caller; pass NULL / 0 to stop recording.
+ * ------------------------------------------------------------------------- */
+#define MOE_STAGE_EVENTS 6
+int moe_set_stage_events(void* const* events, int n_events);
+
+const char* moe_status_string(int status);
+const char* moe_last_error(void); /* thread-local message of the last non-OK return */
+int moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

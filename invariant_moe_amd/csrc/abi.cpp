@@ -1,0 +1,418 @@
+// C ABI: argument validation, workspace carving and kernel launches on the
+// caller's stream.  Declarations and the contract of every entry point are in
+// include/moe.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/moe.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+thread_local void* const* g_stage_events = nullptr;
+thread_local int g_n_stage_events = 0;
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return MOE_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+size_t act_size(moe_dtype a) { return a == MOE_F32 ? 4 : 2; }
+
+// Workspace carving.  Each region starts on a 256-byte boundary.
+struct Carver {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  }
+};
+
+struct LayerLayout {
+  size_t logits, idx, w, mask, wprefix, counts, offsets, row_token, pair_row, h, hs, o, s, total;
+};
+
+LayerLayout layer_layout(int64_t T, int D, int E, int k, int I, int Is, moe_dtype act) {
+  const int64_t R = T * k, W = (T + 63) / 64;
+  const size_t es = act_size(act);
+  Carver c;
+  LayerLayout L;
+  L.logits = c.take((size_t)T * E * 4);
+  L.idx = c.take((size_t)R * 4);
+  L.w = c.take((size_t)R * 4);
+  L.mask = c.take((size_t)E * W * 8);
+  L.wprefix = c.take((size_t)E * W * 4);
+  L.counts = c.take((size_t)E * 4);
+  L.offsets = c.take((size_t)(E + 1) * 4);
+  L.row_token = c.take((size_t)R * 4);
+  L.pair_row = c.take((size_t)R * 4);
+  L.h = c.take((size_t)R * I * es);
+  L.hs = c.take((size_t)T * (Is > 0 ? Is : 0) * es);
+  L.o = c.take((size_t)R * D * es);
+  L.s = c.take((size_t)T * (Is > 0 ? D : 0) * es);
+  L.total = c.off;
+  return L;
+}
+
+int check_dims(int64_t T, int D, int E, int k) {
+  if (T < 0) return fail(MOE_ERR_SHAPE, "T=%lld must be >= 0", (long long)T);
+  if (E < 1 || E > MOE_MAX_EXPERTS)
+    return fail(MOE_ERR_SHAPE, "E=%d must be in [1, %d]", E, MOE_MAX_EXPERTS);
+  if (k < 1 || k > E || k > MOE_MAX_TOPK)
+    return fail(MOE_ERR_SHAPE, "k=%d must be in [1, min(E=%d, %d)]", k, E, MOE_MAX_TOPK);
+  if (D < 32 || D % 32) return fail(MOE_ERR_SHAPE, "D=%d must be a positive multiple of 32", D);
+  if (T * (int64_t)k >= (int64_t)1 << 31) return fail(MOE_ERR_SHAPE, "T*k must be < 2^31");
+  return MOE_OK;
+}
+
+int check_weights(const moe_expert_weights* w, moe_dtype act, const char* which) {
+  if (!w) return fail(MOE_ERR_NULL, "%s weights are NULL", which);
+  if (!w->gate || !w->up || !w->down) return fail(MOE_ERR_NULL, "%s weight pointer is NULL", which);
+  if (!aligned(w->gate, 16) || !aligned(w->up, 16) || !aligned(w->down, 16))
+    return fail(MOE_ERR_ALIGN, "%s weights must be 16-byte aligned", which);
+  if (w->dtype == MOE_MXFP4) {
+    if (act != MOE_BF16) return fail(MOE_ERR_DTYPE, "MXFP4 %s weights need bf16 activations", which);
+    if (!w->gate_scale || !w->up_scale || !w->down_scale)
+      return fail(MOE_ERR_NULL, "MXFP4 %s weights need scale pointers", which);
+  } else {
+    if (w->dtype != act)
+      return fail(MOE_ERR_DTYPE, "%s weight dtype %d does not match activation dtype %d", which,
+                  (int)w->dtype, (int)act);
+    if (w->gate_scale || w->up_scale || w->down_scale)
+      return fail(MOE_ERR_DTYPE, "%s scale pointers must be NULL unless dtype is MXFP4", which);
+  }
+  return MOE_OK;
+}
+
+int check_act(moe_dtype act) {
+  if (act != MOE_F32 && act != MOE_BF16)
+    return fail(MOE_ERR_DTYPE, "activation dtype must be MOE_F32 or MOE_BF16");
+  return MOE_OK;
+}
+
+void record_stage(int i, hipStream_t s) {
+  if (g_stage_events && i < g_n_stage_events && g_stage_events[i])
+    (void)hipEventRecord(static_cast<hipEvent_t>(g_stage_events[i]), s);
+}
+
+moe::GemmSeg make_seg(const void* A, const int32_t* a_index, const int32_t* offsets, int64_t M,
+                      int G, int K, int N, const moe_expert_weights* w, bool gated, void* out) {
+  moe::GemmSeg s{};
+  s.A = A;
+  s.a_index = a_index;
+  s.offsets = offsets;
+  s.M = M;
+  s.G = G;
+  s.K = K;
+  s.N = N;
+  s.W0 = gated ? w->gate : w->down;
+  s.W1 = gated ? w->up : nullptr;
+  s.S0 = gated ? w->gate_scale : w->down_scale;
+  s.S1 = gated ? w->up_scale : nullptr;
+  s.wfmt = w->dtype == MOE_MXFP4 ? 1 : 0;
+  s.out = out;
+  return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_last_error(void) { return g_err; }
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_NULL: return "MOE_ERR_NULL";
+    case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE";
+    case MOE_ERR_DTYPE: return "MOE_ERR_DTYPE";
+    case MOE_ERR_ALIGN: return "MOE_ERR_ALIGN";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "unknown status";
+  }
+}
+
+int moe_set_stage_events(void* const* events, int n_events) {
+  if (n_events < 0) return fail(MOE_ERR_SHAPE, "n_events must be >= 0");
+  g_stage_events = n_events > 0 ? events : nullptr;
+  g_n_stage_events = events ? n_events : 0;
+  return ok();
+}
+
+size_t moe_router_workspace_bytes(int64_t T, int E, moe_route mode) {
+  if (mode == MOE_ROUTE_HASH || T <= 0 || E <= 0) return 0;
+  return align_up((size_t)T * (size_t)E * 4);
+}
+
+int moe_router_topk(const void* x, moe_dtype act, const void* w_router, const float* bias,
+                    const int32_t* token_ids, int64_t T, int D, int E, int k, moe_route mode,
+                    int32_t* topk_idx, float* topk_w, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  int rc;
+  if ((rc = check_dims(T, D, E, k))) return rc;
+  if (mode != MOE_ROUTE_SOFTMAX && mode != MOE_ROUTE_SIGMOID && mode != MOE_ROUTE_HASH)
+    return fail(MOE_ERR_SHAPE, "unknown routing mode %d", (int)mode);
+  if (!topk_idx || !topk_w) return fail(MOE_ERR_NULL, "topk_idx / topk_w are NULL");
+  if (!aligned(topk_idx, 4) || !aligned(topk_w, 4)) return fail(MOE_ERR_ALIGN, "outputs misaligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (mode == MOE_ROUTE_HASH) {
+    if (!token_ids) return fail(MOE_ERR_NULL, "hash routing needs token_ids");
+    if (T == 0) return ok();
+    return hip_status(moe::launch_hash_route(token_ids, T, E, k, topk_idx, topk_w, nullptr, s),
+                      "hash routing");
+  }
+  if ((rc = check_act(act))) return rc;
+  if (!x || !w_router) return fail(MOE_ERR_NULL, "x / w_router are NULL");
+  if (!aligned(x, 16) || !aligned(w_router, 16)) return fail(MOE_ERR_ALIGN, "x / w_router must be 16-byte aligned");
+  if (bias && !aligned(bias, 4)) return fail(MOE_ERR_ALIGN, "bias misaligned");
+  const size_t need = moe_router_workspace_bytes(T, E, mode);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(MOE_ERR_WORKSPACE, "router workspace needs %zu bytes", need);
+  if (workspace && !aligned(workspace, 16)) return fail(MOE_ERR_ALIGN, "workspace misaligned");
+  if (T == 0) return ok();
+  float* logits = static_cast<float*>(workspace);
+  hipError_t e = moe::launch_router_logits(x, act, w_router, T, D, E, logits, s);
+  if (e == hipSuccess) e = moe::launch_topk(logits, bias, T, E, k, mode, topk_idx, topk_w, nullptr, s);
+  return hip_status(e, "router");
+}
+
+int moe_routing_scores(const float* logits, int64_t n, moe_route mode, float* out, void* stream) {
+  if (n < 0) return fail(MOE_ERR_SHAPE, "n must be >= 0");
+  if (mode != MOE_ROUTE_SOFTMAX && mode != MOE_ROUTE_SIGMOID)
+    return fail(MOE_ERR_SHAPE, "routing scores exist for softmax and sigmoid modes only");
+  if (n > 0 && (!logits || !out)) return fail(MOE_ERR_NULL, "NULL argument");
+  if (n > 0 && (!aligned(logits, 4) || !aligned(out, 4))) return fail(MOE_ERR_ALIGN, "misaligned");
+  return hip_status(moe::launch_routing_scores(logits, n, mode, out, static_cast<hipStream_t>(stream)),
+                    "routing scores");
+}
+
+size_t moe_permute_workspace_bytes(int64_t T, int E) {
+  if (T < 0 || E <= 0) return 0;
+  const int64_t W = (T + 63) / 64;
+  Carver c;
+  c.take((size_t)E * W * 8);
+  c.take((size_t)E * W * 4);
+  return c.off;
+}
+
+int moe_permute(const int32_t* topk_idx, int64_t T, int k, int E, int32_t* expert_counts,
+                int32_t* expert_offsets, int32_t* row_token, int32_t* pair_row, const void* x,
+                moe_dtype act, int D, void* x_perm, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  if (T < 0) return fail(MOE_ERR_SHAPE, "T must be >= 0");
+  if (E < 1 || E > MOE_MAX_EXPERTS) return fail(MOE_ERR_SHAPE, "E=%d out of range", E);
+  if (k < 1 || k > E || k > MOE_MAX_TOPK) return fail(MOE_ERR_SHAPE, "k=%d out of range", k);
+  if (T * (int64_t)k >= (int64_t)1 << 31) return fail(MOE_ERR_SHAPE, "T*k must be < 2^31");
+  if (!expert_counts || !expert_offsets || !row_token || !pair_row)
+    return fail(MOE_ERR_NULL, "permutation outputs are NULL");
+  if (T > 0 && !topk_idx) return fail(MOE_ERR_NULL, "topk_idx is NULL");
+  if (x) {
+    int rc;
+    if ((rc = check_act(act))) return rc;
+    if (D < 32 || D % 32) return fail(MOE_ERR_SHAPE, "D=%d must be a positive multiple of 32", D);
+    if (!x_perm) return fail(MOE_ERR_NULL, "x_perm is NULL while x is given");
+    if (!aligned(x, 16) || !aligned(x_perm, 16)) return fail(MOE_ERR_ALIGN, "x / x_perm misaligned");
+  }
+  const size_t need = moe_permute_workspace_bytes(T, E);
+  if (!workspace || workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "permute workspace needs %zu bytes", need);
+  if (!aligned(workspace, 16)) return fail(MOE_ERR_ALIGN, "workspace misaligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t W = (T + 63) / 64;
+  uint64_t* mask = static_cast<uint64_t*>(workspace);
+  int32_t* wprefix = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + align_up((size_t)E * W * 8));
+  hipError_t e = moe::launch_mask_from_idx(topk_idx, T, k, E, mask, s);
+  if (e == hipSuccess)
+    e = moe::launch_permute(topk_idx, T, k, E, mask, wprefix, expert_counts, expert_offsets,
+                            row_token, pair_row, s);
+  if (e == hipSuccess && x)
+    e = moe::launch_gather_rows(x, row_token, T, T * k, (int64_t)D * act_size(act), x_perm, s);
+  return hip_status(e, "permute");
+}
+
+size_t moe_grouped_swiglu_workspace_bytes(int64_t R, int I, moe_dtype act) {
+  if (R <= 0 || I <= 0) return 0;
+  return align_up((size_t)R * I * act_size(act == MOE_F32 ? MOE_F32 : MOE_BF16));
+}
+
+int moe_grouped_swiglu(const void* x_rows, const int32_t* row_index, const int32_t* expert_offsets,
+                       int64_t R, int E, int D, int I, const moe_expert_weights* w, moe_dtype act,
+                       uint32_t flags, void* out, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  int rc;
+  if ((rc = check_act(act))) return rc;
+  if (flags) return fail(MOE_ERR_UNSUPPORTED, "flags 0x%x not supported", flags);
+  if (R < 0 || R >= ((int64_t)1 << 31)) return fail(MOE_ERR_SHAPE, "R out of range");
+  if (E < 1 || E > MOE_MAX_EXPERTS) return fail(MOE_ERR_SHAPE, "E=%d out of range", E);
+  if (D < 32 || D % 32 || I < 32 || I % 32)
+    return fail(MOE_ERR_SHAPE, "D=%d and I=%d must be positive multiples of 32", D, I);
+  if ((rc = check_weights(w, act, "expert"))) return rc;
+  if (!expert_offsets || !out || (R > 0 && !x_rows)) return fail(MOE_ERR_NULL, "NULL argument");
+  if ((x_rows && !aligned(x_rows, 16)) || !aligned(out, 16)) return fail(MOE_ERR_ALIGN, "x_rows / out misaligned");
+  const size_t need = moe_grouped_swiglu_workspace_bytes(R, I, act);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(MOE_ERR_WORKSPACE, "grouped_swiglu workspace needs %zu bytes", need);
+  if (workspace && !aligned(workspace, 16)) return fail(MOE_ERR_ALIGN, "workspace misaligned");
+  if (R == 0) return ok();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t hint = R / E;
+  moe::GemmArgs up{};
+  up.nseg = 1;
+  up.seg[0] = make_seg(x_rows, row_index, expert_offsets, R, E, D, I, w, true, workspace);
+  hipError_t e = moe::launch_grouped_gemm(up, true, act, hint, s);
+  if (e == hipSuccess) {
+    moe::GemmArgs dn{};
+    dn.nseg = 1;
+    dn.seg[0] = make_seg(workspace, nullptr, expert_offsets, R, E, I, D, w, false, out);
+    e = moe::launch_grouped_gemm(dn, false, act, hint, s);
+  }
+  return hip_status(e, "grouped_swiglu");
+}
+
+int moe_combine(const void* expert_out, const int32_t* topk_idx, const float* topk_w,
+                const int32_t* pair_row, const void* shared_out, int64_t T, int k, int D,
+                moe_dtype act, void* y, void* stream) {
+  int rc;
+  if ((rc = check_act(act))) return rc;
+  if (T < 0) return fail(MOE_ERR_SHAPE, "T must be >= 0");
+  if (k < 1 || k > MOE_MAX_TOPK) return fail(MOE_ERR_SHAPE, "k=%d out of range", k);
+  if (D < 32 || D % 32) return fail(MOE_ERR_SHAPE, "D=%d must be a positive multiple of 32", D);
+  if (T > 0 && (!expert_out || !topk_idx || !topk_w || !pair_row || !y))
+    return fail(MOE_ERR_NULL, "NULL argument");
+  if (T > 0 && (!aligned(expert_out, 16) || !aligned(y, 16) ||
+                (shared_out && !aligned(shared_out, 16))))
+    return fail(MOE_ERR_ALIGN, "expert_out / shared_out / y must be 16-byte aligned");
+  return hip_status(moe::launch_combine(expert_out, topk_idx, topk_w, pair_row, shared_out, T, k,
+                                        D, act, y, static_cast<hipStream_t>(stream)),
+                    "combine");
+}
+
+size_t moe_layer_workspace_bytes(int64_t T, int D, int E, int k, int I, int I_shared,
+                                 moe_dtype act, moe_dtype w) {
+  (void)w;
+  if (T < 0 || D <= 0 || E <= 0 || k <= 0 || I <= 0) return 0;
+  return layer_layout(T, D, E, k, I, I_shared, act).total;
+}
+
+int moe_layer_forward(const void* x, const int32_t* token_ids, const void* w_router,
+                      const float* bias, const moe_expert_weights* routed,
+                      const moe_expert_weights* shared, int64_t T, int D, int E, int k, int I,
+                      int I_shared, moe_route mode, moe_dtype act, uint32_t flags, void* y,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  int rc;
+  if ((rc = check_act(act))) return rc;
+  if ((rc = check_dims(T, D, E, k))) return rc;
+  if (flags) return fail(MOE_ERR_UNSUPPORTED, "flags 0x%x not supported", flags);
+  if (I < 32 || I % 32) return fail(MOE_ERR_SHAPE, "I=%d must be a positive multiple of 32", I);
+  if (mode != MOE_ROUTE_SOFTMAX && mode != MOE_ROUTE_SIGMOID && mode != MOE_ROUTE_HASH)
+    return fail(MOE_ERR_SHAPE, "unknown routing mode %d", (int)mode);
+  if ((rc = check_weights(routed, act, "routed"))) return rc;
+  const int Is = shared ? I_shared : 0;
+  if (shared) {
+    if ((rc = check_weights(shared, act, "shared"))) return rc;
+    if (Is < 32 || Is % 32)
+      return fail(MOE_ERR_SHAPE, "I_shared=%d must be a positive multiple of 32", I_shared);
+  }
+  if (T > 0 && (!x || !y)) return fail(MOE_ERR_NULL, "x / y are NULL");
+  if (T > 0 && (!aligned(x, 16) || !aligned(y, 16))) return fail(MOE_ERR_ALIGN, "x / y must be 16-byte aligned");
+  if (mode == MOE_ROUTE_HASH) {
+    if (!token_ids) return fail(MOE_ERR_NULL, "hash routing needs token_ids");
+  } else {
+    if (!w_router) return fail(MOE_ERR_NULL, "w_router is NULL");
+    if (!aligned(w_router, 16)) return fail(MOE_ERR_ALIGN, "w_router must be 16-byte aligned");
+    if (bias && !aligned(bias, 4)) return fail(MOE_ERR_ALIGN, "bias misaligned");
+  }
+  const LayerLayout L = layer_layout(T, D, E, k, I, Is, act);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "layer workspace needs %zu bytes", L.total);
+  if (!aligned(workspace, 256)) return fail(MOE_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if (T == 0) return ok();
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  float* logits = reinterpret_cast<float*>(ws + L.logits);
+  int32_t* idx = reinterpret_cast<int32_t*>(ws + L.idx);
+  float* tw = reinterpret_cast<float*>(ws + L.w);
+  uint64_t* mask = reinterpret_cast<uint64_t*>(ws + L.mask);
+  int32_t* wprefix = reinterpret_cast<int32_t*>(ws + L.wprefix);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  int32_t* row_token = reinterpret_cast<int32_t*>(ws + L.row_token);
+  int32_t* pair_row = reinterpret_cast<int32_t*>(ws + L.pair_row);
+  void* h = ws + L.h;
+  void* hs = ws + L.hs;
+  void* o = ws + L.o;
+  void* sh = ws + L.s;
+  const int64_t R = T * k;
+
+  record_stage(0, s);
+  hipError_t e;
+  if (mode == MOE_ROUTE_HASH) {
+    e = moe::launch_hash_route(token_ids, T, E, k, idx, tw, mask, s);
+  } else {
+    e = moe::launch_router_logits(x, act, w_router, T, D, E, logits, s);
+    if (e == hipSuccess) e = moe::launch_topk(logits, bias, T, E, k, mode, idx, tw, mask, s);
+  }
+  if (e != hipSuccess) return hip_status(e, "routing");
+  record_stage(1, s);
+  e = moe::launch_permute(idx, T, k, E, mask, wprefix, counts, offsets, row_token, pair_row, s);
+  if (e != hipSuccess) return hip_status(e, "permute");
+  record_stage(2, s);
+
+  const int64_t hint = R / E;
+  moe::GemmArgs up{};
+  up.seg[0] = make_seg(x, row_token, offsets, R, E, D, I, routed, true, h);
+  up.nseg = 1;
+  if (shared) {
+    up.seg[1] = make_seg(x, nullptr, nullptr, T, 1, D, Is, shared, true, hs);
+    up.nseg = 2;
+  }
+  e = moe::launch_grouped_gemm(up, true, act, hint, s);
+  if (e != hipSuccess) return hip_status(e, "gate/up GEMM");
+  record_stage(3, s);
+
+  moe::GemmArgs dn{};
+  dn.seg[0] = make_seg(h, nullptr, offsets, R, E, I, D, routed, false, o);
+  dn.nseg = 1;
+  if (shared) {
+    dn.seg[1] = make_seg(hs, nullptr, nullptr, T, 1, Is, D, shared, false, sh);
+    dn.nseg = 2;
+  }
+  e = moe::launch_grouped_gemm(dn, false, act, hint, s);
+  if (e != hipSuccess) return hip_status(e, "down GEMM");
+  record_stage(4, s);
+
+  e = moe::launch_combine(o, idx, tw, pair_row, shared ? sh : nullptr, T, k, D, act, y, s);
+  if (e != hipSuccess) return hip_status(e, "combine");
+  record_stage(5, s);
+  return ok();
+}
+
+}  // extern "C"

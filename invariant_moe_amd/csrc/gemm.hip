@@ -1,0 +1,451 @@
+// Grouped expert GEMMs with the SwiGLU epilogue.
+//
+// Expert FFN: g = W_gate a, u = W_up a, h = SiLU(g) * u, o = W_down h
+// (SwiGLU, "6 基建与训练稳定性优化" section 6.5; gate and up branches, forum
+// article feedbbs.com/linuxdo/72580, GLU section).  Every GEMM sees its whole
+// K in one workgroup (no split sums: the LongCat parity article,
+// "美团把训练和推理的概率做到逐位相同"), so each output element is one fixed
+// chain of MFMA steps over K.
+//
+// Batch invariance.  All bf16 kernels here use ONE instruction,
+// v_mfma_f32_16x16x32_bf16, with the weight tile as operand A (16 output
+// features) and the token tile as operand B (16 rows), K stepped by 32 in
+// increasing order into an accumulator that starts at 0.  An output element
+// depends only on its own weight row and token row and on this fixed chain,
+// never on the other rows of its tile, the tile shape, the number of rows of
+// its expert, or T.  The tile variants below differ only in how many blocks a
+// workgroup holds, so they give identical bits.
+//
+// MXFP4 weights (E2M1 codes + one E8M0 scale per 32 along K; FP4 expert
+// weights, same DeepSeek-V4 page section 6.2) are decoded exactly to bf16 in
+// LDS and then go through the same bf16 MFMA chain, so the result equals the
+// bf16 kernel on the decoded weights bit for bit.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+constexpr int KT = 64;         // K per LDS stage (two MFMA k-steps)
+constexpr int LDK = KT + 8;    // padded LDS row (bf16 elements) -> 144 B stride
+constexpr int MAXG = MOE_MAX_EXPERTS + 1;
+
+// ---------------------------------------------------------------------------
+// Work list: the tiles of all groups of both segments, group-major, then
+// n-tile, then m-tile (m fastest, so neighbouring tiles share weight panels).
+// Every workgroup computes the prefix of tile counts itself from the device
+// row offsets (no host sync, no extra launch).
+// ---------------------------------------------------------------------------
+struct TileInfo {
+  int seg, g;
+  int64_t row0;  // first output row of the tile
+  int rows;      // valid rows in the tile
+  int n0;        // first output feature
+};
+
+// Rows of group g; offsets outside [0, M] or decreasing (outside the
+// contract) give an empty group so no access leaves the row range.
+__device__ __forceinline__ int64_t group_rows(const GemmSeg& s, int g) {
+  if (!s.offsets) return s.M;
+  const int64_t a = s.offsets[g], b = s.offsets[g + 1];
+  return (a < 0 || b > s.M || b < a) ? 0 : b - a;
+}
+
+template <int NT>
+__device__ bool find_tile(const GemmArgs& a, int BM, int BN, int64_t bid, TileInfo& ti,
+                          int64_t* sprefix /* [MAXG + 1] */) {
+  const int G0 = a.seg[0].G;
+  const int Gt = G0 + (a.nseg > 1 ? a.seg[1].G : 0);
+  // per-group tile counts
+  for (int g = threadIdx.x; g < Gt; g += NT) {
+    const GemmSeg& s = (g < G0) ? a.seg[0] : a.seg[1];
+    const int gl = (g < G0) ? g : g - G0;
+    const int64_t M = group_rows(s, gl);
+    const int64_t mt = (M + BM - 1) / BM;
+    const int64_t nt = (s.N + BN - 1) / BN;
+    sprefix[g] = mt * nt;
+  }
+  __syncthreads();
+  // exclusive scan (Gt <= 1025): each thread owns a contiguous run
+  __shared__ int64_t runsum[NT];
+  const int per = (Gt + NT - 1) / NT;
+  const int beg = threadIdx.x * per;
+  const int end = min(beg + per, Gt);
+  int64_t loc = 0;
+  for (int g = beg; g < end; ++g) loc += sprefix[g];
+  runsum[threadIdx.x] = loc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int64_t run = 0;
+    for (int i = 0; i < NT; ++i) {
+      int64_t v = runsum[i];
+      runsum[i] = run;
+      run += v;
+    }
+    sprefix[MAXG] = run;  // total
+  }
+  __syncthreads();
+  int64_t run = runsum[threadIdx.x];
+  for (int g = beg; g < end; ++g) {
+    int64_t v = sprefix[g];
+    sprefix[g] = run;
+    run += v;
+  }
+  __syncthreads();
+  const int64_t total = sprefix[MAXG];
+  const int64_t l = xcd_logical_block(bid, total);
+  if (l < 0) return false;
+  // last group whose prefix <= l (binary search over a non-decreasing array)
+  int lo = 0, hi = Gt - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (sprefix[mid] <= l) lo = mid; else hi = mid - 1;
+  }
+  const int g = lo;
+  const int seg = (g < G0) ? 0 : 1;
+  const int gl = (g < G0) ? g : g - G0;
+  const GemmSeg& s = a.seg[seg];
+  const int64_t M = group_rows(s, gl);
+  const int64_t mt = (M + BM - 1) / BM;
+  const int64_t local = l - sprefix[g];
+  const int64_t ntile = local / mt, mtile = local % mt;
+  ti.seg = seg;
+  ti.g = gl;
+  ti.row0 = (s.offsets ? (int64_t)s.offsets[gl] : 0) + mtile * BM;
+  ti.rows = (int)min((int64_t)BM, M - mtile * BM);
+  ti.n0 = (int)(ntile * BN);
+  return true;
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g / (1.0f + __expf(-g)) * u;
+}
+
+// Exact decode of 32 E2M1 codes (16 bytes, element 2i in the low nibble of
+// byte i) with one E8M0 scale byte into 32 bf16 values.  The product code *
+// 2^(s-127) has at most two significant bits, so it is exact in bf16 for every
+// scale byte <= 252.
+__device__ __forceinline__ void decode_mxfp4_32(const uint4 q, uint32_t sbyte, uint32_t (&o)[16]) {
+  const float scale = sbyte ? __uint_as_float(sbyte << 23) : __uint_as_float(0x00400000u);
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const uint32_t byte = (w[i] >> (8 * b)) & 0xffu;
+      uint32_t pair = 0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t c = (byte >> (4 * h)) & 0xfu;
+        const uint32_t m = c & 7u;
+        const uint32_t mag = m >= 2u ? ((m << 22) + 0x3f000000u) : (m ? 0x3f000000u : 0u);
+        const uint32_t v = __float_as_uint(__uint_as_float(mag) * scale);  // exact
+        pair |= ((v >> 16) | ((c & 8u) << 12)) << (16 * h);
+      }
+      o[i * 4 + b] = pair;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 / MXFP4 MFMA kernel.  BM token rows x BN output features per tile
+// (x2 matrices when GATED: gate rows then up rows in LDS).  Waves form a
+// WM x WN grid; each wave holds TBW token blocks x NBW feature blocks of 16.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int WM, int WN, bool GATED>
+__global__ __launch_bounds__(64 * WM * WN) void k_grouped_gemm_bf16(GemmArgs args) {
+  constexpr int NT = 64 * WM * WN;
+  constexpr int NMAT = GATED ? 2 : 1;
+  constexpr int TBW = BM / 16 / WM;
+  constexpr int NBW = BN / 16 / WN;
+  static_assert(TBW >= 1 && NBW >= 1, "tile too small for the wave grid");
+  constexpr int XCH = BM * (KT / 8);          // 16-byte chunks of the token tile
+  constexpr int WCH = NMAT * BN * (KT / 8);   // 16-byte chunks of the weight tile (bf16)
+  constexpr int QCH = NMAT * BN * 2;          // 16-byte chunks of an MXFP4 weight tile
+  constexpr int XPT = (XCH + NT - 1) / NT;
+  constexpr int WPT = (WCH + NT - 1) / NT;
+  constexpr int QPT = (QCH + NT - 1) / NT;
+
+  __shared__ __align__(16) uint16_t Xs[BM * LDK];
+  __shared__ __align__(16) uint16_t Ws[NMAT * BN * LDK];
+  __shared__ int64_t sprefix[MAXG + 1];
+
+  TileInfo ti;
+  if (!find_tile<NT>(args, BM, BN, blockIdx.x, ti, sprefix)) return;
+  const GemmSeg& s = args.seg[ti.seg];
+  const int K = s.K, N = s.N;
+  const bool fp4 = s.wfmt == 1;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % WM, wn = wave / WM;
+
+  // per-thread source pointers of the token tile (rows clamped into range)
+  const uint16_t* xsrc[XPT];
+#pragma unroll
+  for (int i = 0; i < XPT; ++i) {
+    const int c = tid + i * NT;
+    const int r = min(c / (KT / 8), BM - 1);
+    const int rr = min(r, ti.rows - 1);
+    const int64_t row = ti.row0 + rr;
+    const int64_t src = s.a_index ? (int64_t)s.a_index[row] : row;
+    xsrc[i] = static_cast<const uint16_t*>(s.A) + src * K + (c % (KT / 8)) * 8;
+  }
+  // weight tile sources
+  const uint8_t* wsrc[WPT > QPT ? WPT : QPT];
+  const uint8_t* ssrc[QPT];
+  if (!fp4) {
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) {
+      const int c = min(tid + i * NT, WCH - 1);
+      const int mat = c / (BN * (KT / 8));
+      const int n = (c / (KT / 8)) % BN;
+      const int nn = min(ti.n0 + n, N - 1);
+      const uint16_t* base = static_cast<const uint16_t*>(mat ? s.W1 : s.W0);
+      wsrc[i] = reinterpret_cast<const uint8_t*>(base + ((int64_t)ti.g * N + nn) * K +
+                                                 (c % (KT / 8)) * 8);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+      const int c = min(tid + i * NT, QCH - 1);
+      const int mat = c / (BN * 2);
+      const int n = (c / 2) % BN;
+      const int nn = min(ti.n0 + n, N - 1);
+      const int half = c % 2;
+      const uint8_t* base = static_cast<const uint8_t*>(mat ? s.W1 : s.W0);
+      const uint8_t* sb = mat ? s.S1 : s.S0;
+      const int64_t row = (int64_t)ti.g * N + nn;
+      wsrc[i] = base + row * (K / 2) + half * 16;
+      ssrc[i] = sb + row * (K / 32) + half;
+    }
+  }
+
+  f32x4_t acc[NMAT][NBW][TBW];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+      for (int tb = 0; tb < TBW; ++tb) acc[m][nb][tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  uint4 xr[XPT];
+  uint4 wr[WPT > QPT ? WPT : QPT];
+  uint32_t sr[QPT];
+  const int nk = (K + KT - 1) / KT;
+
+  auto gload = [&](int kt) {
+    const int k0 = kt * KT;
+    const bool half_tile = (k0 + KT > K);  // K % 64 == 32 on the last stage
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      const int c = tid + i * NT;
+      const bool hi = (c % (KT / 8)) >= 4;
+      if (c < XCH && !(half_tile && hi))
+        xr[i] = *reinterpret_cast<const uint4*>(xsrc[i] + k0);
+      else
+        xr[i] = make_uint4(0, 0, 0, 0);
+    }
+    if (!fp4) {
+#pragma unroll
+      for (int i = 0; i < WPT; ++i) {
+        const int c = tid + i * NT;
+        const bool hi = (c % (KT / 8)) >= 4;
+        if (c < WCH && !(half_tile && hi))
+          wr[i] = *reinterpret_cast<const uint4*>(wsrc[i] + (int64_t)k0 * 2);
+        else
+          wr[i] = make_uint4(0, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < QPT; ++i) {
+        const int c = tid + i * NT;
+        const bool hi = (c % 2) == 1;
+        if (c < QCH && !(half_tile && hi)) {
+          wr[i] = *reinterpret_cast<const uint4*>(wsrc[i] + k0 / 2);
+          sr[i] = ssrc[i][k0 / 32];
+        } else {
+          wr[i] = make_uint4(0, 0, 0, 0);
+          sr[i] = 127;
+        }
+      }
+    }
+  };
+  auto lstore = [&]() {
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      const int c = tid + i * NT;
+      if (c < XCH)
+        *reinterpret_cast<uint4*>(&Xs[(c / (KT / 8)) * LDK + (c % (KT / 8)) * 8]) = xr[i];
+    }
+    if (!fp4) {
+#pragma unroll
+      for (int i = 0; i < WPT; ++i) {
+        const int c = tid + i * NT;
+        if (c < WCH)
+          *reinterpret_cast<uint4*>(&Ws[(c / (KT / 8)) * LDK + (c % (KT / 8)) * 8]) = wr[i];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < QPT; ++i) {
+        const int c = tid + i * NT;
+        if (c < QCH) {
+          uint32_t o[16];
+          decode_mxfp4_32(wr[i], sr[i], o);
+          uint4* dst = reinterpret_cast<uint4*>(&Ws[(c / 2) * LDK + (c % 2) * 32]);
+          dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+          dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+          dst[2] = make_uint4(o[8], o[9], o[10], o[11]);
+          dst[3] = make_uint4(o[12], o[13], o[14], o[15]);
+        }
+      }
+    }
+  };
+
+  gload(0);
+  lstore();
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk) gload(kt + 1);
+    const int ksteps = (kt * KT + KT <= K) ? 2 : 1;
+    for (int ks = 0; ks < ksteps; ++ks) {
+      bf16x8_t af[NMAT][NBW], bfr[TBW];
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb) {
+          const int n = m * BN + (wn * NBW + nb) * 16 + (lane & 15);
+          af[m][nb] = *reinterpret_cast<const bf16x8_t*>(&Ws[n * LDK + ks * 32 + 8 * (lane >> 4)]);
+        }
+#pragma unroll
+      for (int tb = 0; tb < TBW; ++tb) {
+        const int r = (wm * TBW + tb) * 16 + (lane & 15);
+        bfr[tb] = *reinterpret_cast<const bf16x8_t*>(&Xs[r * LDK + ks * 32 + 8 * (lane >> 4)]);
+      }
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+          for (int tb = 0; tb < TBW; ++tb)
+            acc[m][nb][tb] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[m][nb], bfr[tb], acc[m][nb][tb], 0, 0, 0);
+    }
+    __syncthreads();
+    if (kt + 1 < nk) {
+      lstore();
+      __syncthreads();
+    }
+  }
+
+  // epilogue: lane holds features n = base + 4*(lane/16) + i (i = 0..3) of
+  // token row base + lane%16 -> one 8-byte store of 4 bf16.
+  uint16_t* out = static_cast<uint16_t*>(s.out);
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+    for (int tb = 0; tb < TBW; ++tb) {
+      const int r = (wm * TBW + tb) * 16 + (lane & 15);
+      const int n = ti.n0 + (wn * NBW + nb) * 16 + 4 * (lane >> 4);
+      if (r < ti.rows && n < N) {
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          v[i] = GATED ? silu_mul(acc[0][nb][tb][i], acc[NMAT - 1][nb][tb][i]) : acc[0][nb][tb][i];
+        uint2 pk = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        *reinterpret_cast<uint2*>(out + (ti.row0 + r) * (int64_t)N + n) = pk;
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 kernel (VALU): each output element is one fmaf chain over K in
+// increasing order from +0, whatever the tile.  Tile 16 rows x 16 features.
+// ---------------------------------------------------------------------------
+template <bool GATED>
+__global__ __launch_bounds__(256) void k_grouped_gemm_f32(GemmArgs args) {
+  constexpr int BM = 16, BN = 16, KC = 32;
+  constexpr int NMAT = GATED ? 2 : 1;
+  __shared__ float As[BM][KC + 1];
+  __shared__ float Bs[NMAT][BN][KC + 1];
+  __shared__ int64_t sprefix[MAXG + 1];
+  TileInfo ti;
+  if (!find_tile<256>(args, BM, BN, blockIdx.x, ti, sprefix)) return;
+  const GemmSeg& s = args.seg[ti.seg];
+  const int K = s.K, N = s.N;
+  const int tid = threadIdx.x;
+  const int r = tid / 16, n = tid % 16;
+  float acc[NMAT];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m) acc[m] = 0.0f;
+  for (int k0 = 0; k0 < K; k0 += KC) {
+    __syncthreads();
+    for (int i = tid; i < BM * KC; i += 256) {
+      const int rr = min(i / KC, ti.rows - 1), kk = i % KC;
+      const int64_t row = ti.row0 + rr;
+      const int64_t src = s.a_index ? (int64_t)s.a_index[row] : row;
+      As[i / KC][kk] = (k0 + kk < K) ? static_cast<const float*>(s.A)[src * K + k0 + kk] : 0.0f;
+    }
+    for (int i = tid; i < NMAT * BN * KC; i += 256) {
+      const int m = i / (BN * KC), nn = min(ti.n0 + (i / KC) % BN, N - 1), kk = i % KC;
+      const float* W = static_cast<const float*>(m ? s.W1 : s.W0);
+      Bs[m][(i / KC) % BN][kk] = (k0 + kk < K) ? W[((int64_t)ti.g * N + nn) * K + k0 + kk] : 0.0f;
+    }
+    __syncthreads();
+    const int kc = min(KC, K - k0);
+    for (int kk = 0; kk < kc; ++kk)
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) acc[m] = __builtin_fmaf(As[r][kk], Bs[m][n][kk], acc[m]);
+  }
+  if (r < ti.rows && ti.n0 + n < N) {
+    const float v = GATED ? acc[0] / (1.0f + expf(-acc[0])) * acc[NMAT - 1] : acc[0];
+    static_cast<float*>(s.out)[(ti.row0 + r) * (int64_t)N + ti.n0 + n] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launch: grid = an upper bound of the tile count (rounded to the 8 XCDs);
+// workgroups past the real count exit after the prefix.
+// ---------------------------------------------------------------------------
+static int64_t seg_tile_bound(const GemmSeg& s, int BM, int BN) {
+  const int64_t nt = (s.N + BN - 1) / BN;
+  if (!s.offsets) return ((s.M + BM - 1) / BM) * nt;
+  // sum_g ceil(M_g/BM) <= ceil(R/BM) + (number of non-empty groups)
+  const int64_t R = s.M;  // total rows of the segment
+  const int64_t nonempty = R < s.G ? R : s.G;
+  return ((R + BM - 1) / BM + nonempty) * nt;
+}
+
+template <int BM, int BN, int WM, int WN>
+static hipError_t launch_bf16_cfg(const GemmArgs& a, bool gated, hipStream_t st) {
+  int64_t tiles = 0;
+  for (int i = 0; i < a.nseg; ++i) tiles += seg_tile_bound(a.seg[i], BM, BN);
+  if (tiles == 0) return hipSuccess;
+  const int64_t grid = (tiles + 7) / 8 * 8;
+  if (gated)
+    hipLaunchKernelGGL((k_grouped_gemm_bf16<BM, BN, WM, WN, true>), dim3((unsigned)grid),
+                       dim3(64 * WM * WN), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_grouped_gemm_bf16<BM, BN, WM, WN, false>), dim3((unsigned)grid),
+                       dim3(64 * WM * WN), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_grouped_gemm(const GemmArgs& a, bool gated, int act, int64_t rows_per_group_hint,
+                               hipStream_t st) {
+  if (act == MOE_F32) {
+    int64_t tiles = 0;
+    for (int i = 0; i < a.nseg; ++i) tiles += seg_tile_bound(a.seg[i], 16, 16);
+    if (tiles == 0) return hipSuccess;
+    const int64_t grid = (tiles + 7) / 8 * 8;
+    if (gated)
+      hipLaunchKernelGGL(k_grouped_gemm_f32<true>, dim3((unsigned)grid), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL(k_grouped_gemm_f32<false>, dim3((unsigned)grid), dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
+  // Tile shape from the average rows per group (host-side, no sync).  Every
+  // variant computes identical bits (same MFMA chain per element).
+  if (rows_per_group_hint <= 16) return launch_bf16_cfg<16, 64, 1, 4>(a, gated, st);
+  if (rows_per_group_hint <= 64) return launch_bf16_cfg<64, 64, 4, 1>(a, gated, st);
+  return launch_bf16_cfg<128, 64, 4, 1>(a, gated, st);
+}
+
+}  // namespace moe

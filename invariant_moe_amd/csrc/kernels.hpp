@@ -1,0 +1,53 @@
+// Internal launch interface between the C-ABI host code and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// One segment of a grouped GEMM: G groups of rows that share the reduction
+// input layout; group g uses weights [g] of W0/W1 (and scales S0/S1).
+struct GemmSeg {
+  const void* A;           // reduction input rows [*, K] (bf16 bits or fp32)
+  const int32_t* a_index;  // output row r reads A[a_index[r]] (nullptr: A[r])
+  const int32_t* offsets;  // [G+1] device row offsets (nullptr: one group of M rows)
+  int64_t M;               // total rows of the segment (= offsets[G] when offsets != nullptr)
+  int G;
+  int K, N;
+  const void* W0;          // [G, N, K] gate (gated) or down; MXFP4: codes [G, N, K/2]
+  const void* W1;          // [G, N, K] up (gated only)
+  const uint8_t* S0;       // MXFP4 scales [G, N, K/32]
+  const uint8_t* S1;
+  int wfmt;                // 0 bf16/fp32 (as act), 1 MXFP4
+  void* out;               // [rows, N]
+};
+
+struct GemmArgs {
+  GemmSeg seg[2];
+  int nseg;
+};
+
+hipError_t launch_router_logits(const void* x, int act, const void* w, int64_t T, int D, int E,
+                                float* logits, hipStream_t s);
+hipError_t launch_topk(const float* logits, const float* bias, int64_t T, int E, int k, int mode,
+                       int32_t* idx, float* w, uint64_t* mask, hipStream_t s);
+hipError_t launch_hash_route(const int32_t* token_ids, int64_t T, int E, int k, int32_t* idx,
+                             float* w, uint64_t* mask, hipStream_t s);
+hipError_t launch_routing_scores(const float* in, int64_t n, int mode, float* out, hipStream_t s);
+hipError_t launch_mask_from_idx(const int32_t* topk_idx, int64_t T, int k, int E, uint64_t* mask,
+                                hipStream_t s);
+hipError_t launch_permute(const int32_t* topk_idx, int64_t T, int k, int E, const uint64_t* mask,
+                          int32_t* wprefix, int32_t* counts, int32_t* offsets, int32_t* row_token,
+                          int32_t* pair_row, hipStream_t s);
+hipError_t launch_gather_rows(const void* x, const int32_t* row_token, int64_t T, int64_t R,
+                              int64_t row_bytes, void* out, hipStream_t s);
+hipError_t launch_grouped_gemm(const GemmArgs& a, bool gated, int act,
+                               int64_t rows_per_group_hint, hipStream_t s);
+hipError_t launch_combine(const void* expert_out, const int32_t* topk_idx, const float* topk_w,
+                          const int32_t* pair_row, const void* shared_out, int64_t T, int k,
+                          int D, int act, void* y, hipStream_t s);
+
+}  // namespace moe
