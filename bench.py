@@ -1,0 +1,284 @@
+"""Benchmark of the batch-invariant MoE layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config N] [--T T]
+
+A step is one moe_layer_forward (routing, permutation, gate/up SwiGLU GEMM,
+down GEMM, combine) over one batch of seeded synthetic tokens whose inputs are
+already resident in HBM.  The default workload is the small bf16 layer
+(T=512, D=1024, E=64 routed + 1 shared expert, top-6 sigmoid routing, expert
+inter dim 512).  Several replicas of the expert weights are rotated across
+steps so that the 256 MB last-level cache cannot hold the weights between
+steps.
+
+Prints ONE JSON line with throughput (tokens/s), the roofline of the dominant
+kernel (the gate/up SwiGLU GEMM) measured with HIP events recorded between the
+stages of every timed step, and the CPU oracle timed on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "gate_up_gemm_traffic.json")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--config", type=int, default=2, help="layer recipe (1..5), default 2")
+    p.add_argument("--T", type=int, default=None, help="override the batch size")
+    p.add_argument("--replicas", type=int, default=0, help="weight replicas (0 = auto)")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="approximate CPU time budget of the oracle baseline (0 = skip)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 1 GiB device copy (counter calibration)")
+    return p.parse_args()
+
+
+class Hip:
+    """hipEvent helpers through the HIP runtime (events live on the caller's stream)."""
+
+    def __init__(self):
+        self.L = ctypes.CDLL("libamdhip64.so")
+        self.L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.L.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                               ctypes.c_void_p]
+        self.L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.L.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def record(self, e, stream):
+        assert self.L.hipEventRecord(e, stream) == 0
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        assert self.L.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "common.hpp", "kernels.hpp"):
+        with open(os.path.join(ROOT, "invariant_moe_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(per_launch_bytes_alg: float):
+    """HBM bytes per launch of the gate/up GEMM from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source."""
+    try:
+        with open(PROFILE_TRAFFIC) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("bytes_per_launch")
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); "
+              "the multi-GPU sharding is described in DESIGN.md, not run.", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import numpy as np
+    import torch
+
+    import invariant_moe_amd as moe
+    import synth
+    from synth import device as sdev
+
+    cfg = synth.CONFIGS[args.config]
+    if args.T is not None:
+        cfg = cfg.with_T(args.T)
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+    hip = Hip()
+
+    print(f"[bench] uploading recipe {cfg.cid} ({cfg.name}) T={cfg.T}", file=sys.stderr, flush=True)
+    dl = sdev.upload_layer(cfg, dev)
+    wbytes_routed = dl.gate.numel() * dl.gate.element_size() * 3  # gate + up + down (+pack)
+    if dl.gate_scale is not None:
+        wbytes_routed += 3 * dl.gate_scale.numel()
+    # replicas so the weights do not stay in the 256 MB last-level cache
+    nrep = args.replicas or max(1, min(8, int(np.ceil(1.2e9 / max(wbytes_routed, 1)))))
+    layers = [sdev.layer_object(dl)]
+    for _ in range(nrep - 1):
+        c = sdev.DeviceLayer(cfg, dl.w_router, dl.bias, dl.gate.clone(), dl.up.clone(),
+                             dl.down.clone(),
+                             None if dl.gate_scale is None else dl.gate_scale.clone(),
+                             None if dl.up_scale is None else dl.up_scale.clone(),
+                             None if dl.down_scale is None else dl.down_scale.clone(),
+                             None if dl.sh_gate is None else dl.sh_gate.clone(),
+                             None if dl.sh_up is None else dl.sh_up.clone(),
+                             None if dl.sh_down is None else dl.sh_down.clone())
+        layers.append(sdev.layer_object(c))
+    x = sdev.x_device(cfg, dev)
+    ids = sdev.token_ids_device(cfg, dev)
+    y = torch.empty((cfg.T, cfg.D), dtype=x.dtype, device=dev)
+
+    # routing statistics of this batch (for the algorithmic byte count)
+    idx, _ = moe.router_topk(x, dl.w_router, dl.bias, ids, cfg.E, cfg.k, cfg.route)
+    counts = torch.bincount(idx.flatten().long(), minlength=cfg.E).cpu().numpy()
+    U = int((counts > 0).sum())
+
+    for i in range(args.warmup):
+        layers[i % nrep].forward(x, ids, out=y)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[hip.event() for _ in range(6)] for _ in range(K)]
+    ev0, ev1 = hip.event(), hip.event()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    hip.record(ev0, sptr)
+    for i in range(K):
+        moe.set_stage_events(evs[i])
+        layers[i % nrep].forward(x, ids, out=y)
+    moe.set_stage_events(None)
+    hip.record(ev1, sptr)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = hip.elapsed_ms(ev0, ev1)
+    ms_per_step = max(wall * 1e3, gpu_ms) / K
+
+    stage_ms = np.array([[hip.elapsed_ms(evs[i][s], evs[i][s + 1]) for s in range(5)]
+                         for i in range(K)])
+    stage_avg = stage_ms.mean(0)
+    gu_ms = float(stage_avg[2])
+
+    # algorithmic work of the gate/up SwiGLU GEMM launch (routed + shared groups)
+    T, D, E, k, I, Is = cfg.T, cfg.D, cfg.E, cfg.k, cfg.I, cfg.I_shared
+    R = T * k
+    es = 4 if cfg.act == "f32" else 2
+    if cfg.wdtype == "mxfp4":
+        w_gu = U * 2 * I * (D // 2 + D // 32)
+    else:
+        w_gu = U * 2 * I * D * es
+    w_gu += 2 * Is * D * es
+    gu_bytes = w_gu + T * D * es + (R * I + T * Is) * es
+    gu_flops = 4 * R * D * I + 4 * T * D * Is
+    achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
+    traffic = measured_traffic(gu_bytes)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "kernel": "k_grouped_gemm_bf16 (gate/up + SwiGLU)",
+                "alg_bytes_per_launch": int(gu_bytes),
+                "avg_launch_ms": round(gu_ms, 5),
+                "mfma_tflops": round(gu_flops / (gu_ms * 1e-3) / 1e12, 2),
+                "mfma_frac": round(gu_flops / (gu_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    if cfg.act == "f32":
+        roofline["bound"] = "hbm"
+
+    # whole-layer algorithmic traffic (touched experts once, shared, router, x, y)
+    layer_w = w_gu * 3 // 2 if cfg.wdtype != "mxfp4" else U * 3 * I * (D // 2 + D // 32) + 3 * Is * D * es
+    layer_bytes = layer_w + (E * D * es if cfg.route != "hash" else 0) + 2 * T * D * es
+    layer_flops = 6 * R * D * I + 6 * T * D * Is + (2 * T * D * E if cfg.route != "hash" else 0)
+
+    # CPU oracle on the host cores (bounded sample of the same workload)
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+        xs = synth.x_tokens(cfg)
+        idsn = synth.token_ids(cfg) if cfg.route == "hash" else None
+        T_s = cfg.T
+        if cfg.D * cfg.I * cfg.k > 1 << 26:  # large layers: a 16-token slice
+            T_s = min(16, cfg.T)
+            xs = np.ascontiguousarray(xs[:T_s])
+            idsn = None if idsn is None else np.ascontiguousarray(idsn[:T_s])
+        lg_idx = None
+        experts = {}
+        if cfg.route == "hash":
+            lg_idx, _ = oracle.route(None, None, idsn, T_s, E, k, "hash")
+        else:
+            lg = oracle.router_logits(xs, synth.router_weight(cfg))
+            lg_idx, _ = oracle.route(lg, synth.router_bias(cfg), None, T_s, E, k, cfg.route)
+        for e in np.unique(lg_idx):
+            experts[int(e)] = synth.expert_matrices(cfg, int(e))
+        wr = synth.router_weight(cfg) if cfg.route != "hash" else None
+        bias = synth.router_bias(cfg)
+        sh = synth.shared_matrices(cfg)
+        runs, t_cpu = 0, 0.0
+        while runs == 0 or t_cpu < args.cpu_seconds:
+            c0 = time.perf_counter()
+            oracle.layer_forward(xs, idsn, wr, bias, experts, sh, T_s, D, E, k, I,
+                                 Is, cfg.route, cfg.wdtype)
+            t_cpu += time.perf_counter() - c0
+            runs += 1
+        cpu = {"value": round(runs * T_s / t_cpu, 2), "unit": "tokens/s",
+               "cores": oracle.num_threads(), "kind": "oracle",
+               "sample": f"{runs} x oracle layer forward of {T_s} tokens of the same recipe "
+                         f"({t_cpu:.1f} s)"}
+
+    tokens_per_s = cfg.T / (ms_per_step * 1e-3)
+    out = {
+        "metric": "MoE-layer tokens/s; %MFMA peak (prefill), %HBM GB/s (decode)",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if cfg.act == "f32" else "bf16",
+        "data": "synthetic (seeded Philox inputs of the recipe's shapes and distributions)",
+        "config": {"workload": f"MoE layer recipe {cfg.cid} ({cfg.name}): T={T}, D={D}, E={E} "
+                               f"routed + {1 if Is else 0} shared, top-{k} {cfg.route}, I={I}, "
+                               f"I_shared={Is}, weights {cfg.wdtype}",
+                   "T": T, "D": D, "E": E, "k": k, "I": I, "I_shared": Is,
+                   "routing": cfg.route, "weights": cfg.wdtype, "parallelism": "single GPU",
+                   "weight_replicas": nrep, "experts_touched": U,
+                   "max_rows_per_expert": int(counts.max())},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "layer": {"alg_bytes": int(layer_bytes), "flops": int(layer_flops),
+                  "gbs": round(layer_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+                  "hbm_frac": round(layer_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                  "tflops": round(layer_flops / (ms_per_step * 1e-3) / 1e12, 2),
+                  "stage_ms": {n: round(float(v), 5) for n, v in zip(moe.STAGES, stage_avg)},
+                  "gpu_event_ms_per_step": round(gpu_ms / K, 5)},
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -198,7 +198,7 @@ int moe_router_topk(const void* x, moe_dtype act, const void* w_router, const fl
   if (workspace && !aligned(workspace, 16)) return fail(MOE_ERR_ALIGN, "workspace misaligned");
   if (T == 0) return ok();
   float* logits = static_cast<float*>(workspace);
-  hipError_t e = moe::launch_router_logits(x, act, w_router, T, D, E, logits, s);
+  hipError_t e = moe::launch_router_logits(x, act, w_router, T, D, E, logits, nullptr, s);
   if (e == hipSuccess) e = moe::launch_topk(logits, bias, T, E, k, mode, topk_idx, topk_w, nullptr, s);
   return hip_status(e, "router");
 }
@@ -377,7 +377,7 @@ int moe_layer_forward(const void* x, const int32_t* token_ids, const void* w_rou
   if (mode == MOE_ROUTE_HASH) {
     e = moe::launch_hash_route(token_ids, T, E, k, idx, tw, mask, s);
   } else {
-    e = moe::launch_router_logits(x, act, w_router, T, D, E, logits, s);
+    e = moe::launch_router_logits(x, act, w_router, T, D, E, logits, mask, s);
     if (e == hipSuccess) e = moe::launch_topk(logits, bias, T, E, k, mode, idx, tw, mask, s);
   }
   if (e != hipSuccess) return hip_status(e, "routing");

@@ -40,20 +40,24 @@ struct Row8<float> {
   }
 };
 
-// One workgroup per token; each thread owns 8 consecutive features.
+// TPT threads per token (a power of two covering D/8, at most 256), 256/TPT
+// tokens per workgroup; each thread owns 8 consecutive features per pass.
 template <typename ACT>
 __global__ __launch_bounds__(256) void k_combine(const ACT* __restrict__ eo,
                                                  const int32_t* __restrict__ topk_idx,
                                                  const float* __restrict__ topk_w,
                                                  const int32_t* __restrict__ pair_row,
                                                  const ACT* __restrict__ shared, int64_t T, int k,
-                                                 int D, ACT* __restrict__ y) {
-  __shared__ int64_t s_row[MOE_MAX_TOPK];
-  __shared__ float s_w[MOE_MAX_TOPK];
-  const int64_t t = blockIdx.x;
-  if (threadIdx.x < k) {
-    // position of this slot in ascending expert id (ids are distinct)
-    const int j = threadIdx.x;
+                                                 int D, int TPT, ACT* __restrict__ y) {
+  __shared__ int64_t s_rows[256 / 64][MOE_MAX_TOPK];
+  __shared__ float s_ws[256 / 64][MOE_MAX_TOPK];
+  const int sub = threadIdx.x / TPT, lt = threadIdx.x % TPT;
+  const int64_t t = (int64_t)blockIdx.x * (256 / TPT) + sub;
+  int64_t* s_row = s_rows[sub];
+  float* s_w = s_ws[sub];
+  if (t < T && lt < k) {
+    // position of this slot in ascending expert id
+    const int j = lt;
     const int e = topk_idx[t * k + j];
     int pos = 0;  // rank by (expert id, slot): a permutation even for repeated ids
     for (int q = 0; q < k; ++q) {
@@ -67,7 +71,8 @@ __global__ __launch_bounds__(256) void k_combine(const ACT* __restrict__ eo,
     s_w[pos] = topk_w[t * k + j];
   }
   __syncthreads();
-  for (int d = threadIdx.x * 8; d < D; d += 256 * 8) {
+  if (t >= T) return;
+  for (int d = lt * 8; d < D; d += TPT * 8) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int q = 0; q < k; ++q) {
       float v[8];
@@ -90,13 +95,16 @@ hipError_t launch_combine(const void* eo, const int32_t* topk_idx, const float* 
                           const int32_t* pair_row, const void* shared, int64_t T, int k, int D,
                           int act, void* y, hipStream_t s) {
   if (T == 0) return hipSuccess;
+  int tpt = 64;  // >= k (k <= 32) so the slot setup fits in one token's threads
+  while (tpt < 256 && tpt * 8 < D) tpt *= 2;
+  const unsigned grid = (unsigned)((T + (256 / tpt) - 1) / (256 / tpt));
   if (act == MOE_BF16)
-    hipLaunchKernelGGL(k_combine<uint16_t>, dim3((unsigned)T), dim3(256), 0, s,
-                       (const uint16_t*)eo, topk_idx, topk_w, pair_row, (const uint16_t*)shared, T,
-                       k, D, (uint16_t*)y);
+    hipLaunchKernelGGL(k_combine<uint16_t>, dim3(grid), dim3(256), 0, s, (const uint16_t*)eo,
+                       topk_idx, topk_w, pair_row, (const uint16_t*)shared, T, k, D, tpt,
+                       (uint16_t*)y);
   else
-    hipLaunchKernelGGL(k_combine<float>, dim3((unsigned)T), dim3(256), 0, s, (const float*)eo,
-                       topk_idx, topk_w, pair_row, (const float*)shared, T, k, D, (float*)y);
+    hipLaunchKernelGGL(k_combine<float>, dim3(grid), dim3(256), 0, s, (const float*)eo, topk_idx,
+                       topk_w, pair_row, (const float*)shared, T, k, D, tpt, (float*)y);
   return hipGetLastError();
 }
 

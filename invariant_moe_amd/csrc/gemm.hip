@@ -20,6 +20,8 @@
 // weights, same DeepSeek-V4 page section 6.2) are decoded exactly to bf16 in
 // LDS and then go through the same bf16 MFMA chain, so the result equals the
 // bf16 kernel on the decoded weights bit for bit.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -52,7 +54,7 @@ __device__ __forceinline__ int64_t group_rows(const GemmSeg& s, int g) {
 
 template <int NT>
 __device__ bool find_tile(const GemmArgs& a, int BM, int BN, int64_t bid, TileInfo& ti,
-                          int64_t* sprefix /* [MAXG + 1] */) {
+                          int64_t* sprefix /* [MAXG + 1] */, int64_t* runsum /* [NT] */) {
   const int G0 = a.seg[0].G;
   const int Gt = G0 + (a.nseg > 1 ? a.seg[1].G : 0);
   // per-group tile counts
@@ -65,28 +67,27 @@ __device__ bool find_tile(const GemmArgs& a, int BM, int BN, int64_t bid, TileIn
     sprefix[g] = mt * nt;
   }
   __syncthreads();
-  // exclusive scan (Gt <= 1025): each thread owns a contiguous run
-  __shared__ int64_t runsum[NT];
+  // exclusive scan (Gt <= 1025): each thread owns a contiguous run; run sums
+  // are scanned with wave shuffles, then across the NT/64 waves.
   const int per = (Gt + NT - 1) / NT;
   const int beg = threadIdx.x * per;
   const int end = min(beg + per, Gt);
   int64_t loc = 0;
   for (int g = beg; g < end; ++g) loc += sprefix[g];
-  runsum[threadIdx.x] = loc;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int64_t run = 0;
-    for (int i = 0; i < NT; ++i) {
-      int64_t v = runsum[i];
-      runsum[i] = run;
-      run += v;
-    }
-    sprefix[MAXG] = run;  // total
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int64_t incl = loc;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const int64_t o = __shfl_up(incl, m);
+    if (lane >= m) incl += o;
   }
+  if (lane == 63) runsum[wave] = incl;
   __syncthreads();
-  int64_t run = runsum[threadIdx.x];
+  int64_t run = incl - loc;
+  for (int w = 0; w < wave; ++w) run += runsum[w];
+  if (threadIdx.x == NT - 1) sprefix[MAXG] = run + loc;  // total
   for (int g = beg; g < end; ++g) {
-    int64_t v = sprefix[g];
+    const int64_t v = sprefix[g];
     sprefix[g] = run;
     run += v;
   }
@@ -151,7 +152,7 @@ __device__ __forceinline__ void decode_mxfp4_32(const uint4 q, uint32_t sbyte, u
 // (x2 matrices when GATED: gate rows then up rows in LDS).  Waves form a
 // WM x WN grid; each wave holds TBW token blocks x NBW feature blocks of 16.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, bool GATED>
+template <int BM, int BN, int WM, int WN, int P, bool GATED, bool FP4>
 __global__ __launch_bounds__(64 * WM * WN) void k_grouped_gemm_bf16(GemmArgs args) {
   constexpr int NT = 64 * WM * WN;
   constexpr int NMAT = GATED ? 2 : 1;
@@ -164,16 +165,23 @@ __global__ __launch_bounds__(64 * WM * WN) void k_grouped_gemm_bf16(GemmArgs arg
   constexpr int XPT = (XCH + NT - 1) / NT;
   constexpr int WPT = (WCH + NT - 1) / NT;
   constexpr int QPT = (QCH + NT - 1) / NT;
-
-  __shared__ __align__(16) uint16_t Xs[BM * LDK];
-  __shared__ __align__(16) uint16_t Ws[NMAT * BN * LDK];
-  __shared__ int64_t sprefix[MAXG + 1];
+  constexpr int WQ = FP4 ? QPT : WPT;
+  constexpr int BUF = (BM + NMAT * BN) * LDK;  // bf16 elements of one LDS stage
+  constexpr int TILE_BYTES = 2 * BUF * 2;
+  constexpr int PREFIX_BYTES = (MAXG + 1 + NT) * 8;
+  constexpr int SMEM = TILE_BYTES > PREFIX_BYTES ? TILE_BYTES : PREFIX_BYTES;
+  __shared__ __align__(16) unsigned char smem[SMEM];
 
   TileInfo ti;
-  if (!find_tile<NT>(args, BM, BN, blockIdx.x, ti, sprefix)) return;
+  {
+    int64_t* sprefix = reinterpret_cast<int64_t*>(smem);
+    if (!find_tile<NT>(args, BM, BN, blockIdx.x, ti, sprefix, sprefix + MAXG + 1)) return;
+    __syncthreads();  // the prefix area is reused for the tiles below
+  }
+  uint16_t* lds = reinterpret_cast<uint16_t*>(smem);  // [2][BM + NMAT*BN][LDK]
   const GemmSeg& s = args.seg[ti.seg];
   const int K = s.K, N = s.N;
-  const bool fp4 = s.wfmt == 1;
+  constexpr bool fp4 = FP4;  // weight format of this instantiation (the launcher splits segments)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % WM, wn = wave / WM;
 
@@ -189,9 +197,9 @@ __global__ __launch_bounds__(64 * WM * WN) void k_grouped_gemm_bf16(GemmArgs arg
     xsrc[i] = static_cast<const uint16_t*>(s.A) + src * K + (c % (KT / 8)) * 8;
   }
   // weight tile sources
-  const uint8_t* wsrc[WPT > QPT ? WPT : QPT];
+  const uint8_t* wsrc[WQ];
   const uint8_t* ssrc[QPT];
-  if (!fp4) {
+  if constexpr (!fp4) {
 #pragma unroll
     for (int i = 0; i < WPT; ++i) {
       const int c = min(tid + i * NT, WCH - 1);
@@ -226,61 +234,70 @@ __global__ __launch_bounds__(64 * WM * WN) void k_grouped_gemm_bf16(GemmArgs arg
 #pragma unroll
       for (int tb = 0; tb < TBW; ++tb) acc[m][nb][tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  uint4 xr[XPT];
-  uint4 wr[WPT > QPT ? WPT : QPT];
-  uint32_t sr[QPT];
+  // P register stages in flight; LDS holds two stages.
+  uint4 xr[P][XPT];
+  uint4 wr[P][WQ];
+  uint32_t sr[P][QPT];
   const int nk = (K + KT - 1) / KT;
 
-  auto gload = [&](int kt) {
+  // Branch-free stage load (every lane always issues the same loads, from
+  // clamped in-range addresses; out-of-tile parts are zeroed afterwards), so
+  // the compiler can wait for exactly one stage while P-1 stay in flight.
+  // Stage load.  In the pipelined loop (half == false) every lane issues the
+  // same unconditional loads (lanes without a chunk read a clamped in-range
+  // address and skip the LDS store), so the compiler can wait for exactly one
+  // stage while the others stay in flight.  half == true loads the first 32
+  // k of the last stage when K % 64 == 32 and zeroes the rest.
+  auto gload = [&](uint4 (&xq)[XPT], uint4 (&wq)[WQ], uint32_t (&sq)[QPT], int kt, bool half) {
     const int k0 = kt * KT;
-    const bool half_tile = (k0 + KT > K);  // K % 64 == 32 on the last stage
+    const bool none = half && (K % KT) == 0;  // trailing step over zeros
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
       const int c = tid + i * NT;
-      const bool hi = (c % (KT / 8)) >= 4;
-      if (c < XCH && !(half_tile && hi))
-        xr[i] = *reinterpret_cast<const uint4*>(xsrc[i] + k0);
+      if (half && (none || (c % (KT / 8)) >= 4))
+        xq[i] = make_uint4(0, 0, 0, 0);
       else
-        xr[i] = make_uint4(0, 0, 0, 0);
+        xq[i] = *reinterpret_cast<const uint4*>(xsrc[i] + k0);
     }
-    if (!fp4) {
+    if constexpr (!fp4) {
 #pragma unroll
       for (int i = 0; i < WPT; ++i) {
         const int c = tid + i * NT;
-        const bool hi = (c % (KT / 8)) >= 4;
-        if (c < WCH && !(half_tile && hi))
-          wr[i] = *reinterpret_cast<const uint4*>(wsrc[i] + (int64_t)k0 * 2);
+        if (half && (none || (c % (KT / 8)) >= 4))
+          wq[i] = make_uint4(0, 0, 0, 0);
         else
-          wr[i] = make_uint4(0, 0, 0, 0);
+          wq[i] = *reinterpret_cast<const uint4*>(wsrc[i] + (int64_t)k0 * 2);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < QPT; ++i) {
         const int c = tid + i * NT;
-        const bool hi = (c % 2) == 1;
-        if (c < QCH && !(half_tile && hi)) {
-          wr[i] = *reinterpret_cast<const uint4*>(wsrc[i] + k0 / 2);
-          sr[i] = ssrc[i][k0 / 32];
+        if (half && (none || (c % 2) == 1)) {
+          wq[i] = make_uint4(0, 0, 0, 0);
+          sq[i] = 127u;
         } else {
-          wr[i] = make_uint4(0, 0, 0, 0);
-          sr[i] = 127;
+          wq[i] = *reinterpret_cast<const uint4*>(wsrc[i] + k0 / 2);
+          sq[i] = ssrc[i][k0 / 32];
         }
       }
     }
   };
-  auto lstore = [&]() {
+  auto lstore = [&](const uint4 (&xq)[XPT], const uint4 (&wq)[WQ], const uint32_t (&sq)[QPT],
+                    int buf) {
+    uint16_t* Xs = lds + buf * BUF;
+    uint16_t* Ws = Xs + BM * LDK;
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
       const int c = tid + i * NT;
       if (c < XCH)
-        *reinterpret_cast<uint4*>(&Xs[(c / (KT / 8)) * LDK + (c % (KT / 8)) * 8]) = xr[i];
+        *reinterpret_cast<uint4*>(&Xs[(c / (KT / 8)) * LDK + (c % (KT / 8)) * 8]) = xq[i];
     }
-    if (!fp4) {
+    if constexpr (!fp4) {
 #pragma unroll
       for (int i = 0; i < WPT; ++i) {
         const int c = tid + i * NT;
         if (c < WCH)
-          *reinterpret_cast<uint4*>(&Ws[(c / (KT / 8)) * LDK + (c % (KT / 8)) * 8]) = wr[i];
+          *reinterpret_cast<uint4*>(&Ws[(c / (KT / 8)) * LDK + (c % (KT / 8)) * 8]) = wq[i];
       }
     } else {
 #pragma unroll
@@ -288,7 +305,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_grouped_gemm_bf16(GemmArgs arg
         const int c = tid + i * NT;
         if (c < QCH) {
           uint32_t o[16];
-          decode_mxfp4_32(wr[i], sr[i], o);
+          decode_mxfp4_32(wq[i], sq[i], o);
           uint4* dst = reinterpret_cast<uint4*>(&Ws[(c / 2) * LDK + (c % 2) * 32]);
           dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
           dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
@@ -298,14 +315,14 @@ __global__ __launch_bounds__(64 * WM * WN) void k_grouped_gemm_bf16(GemmArgs arg
       }
     }
   };
-
-  gload(0);
-  lstore();
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) gload(kt + 1);
-    const int ksteps = (kt * KT + KT <= K) ? 2 : 1;
-    for (int ks = 0; ks < ksteps; ++ks) {
+  // The fixed per-element chain: for each 32-wide k-step in increasing order,
+  // acc = mfma(weights, tokens, acc).
+  auto compute = [&](int buf, auto ksteps_c) {
+    constexpr int KSTEPS = decltype(ksteps_c)::value;
+    const uint16_t* Xs = lds + buf * BUF;
+    const uint16_t* Ws = Xs + BM * LDK;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
       bf16x8_t af[NMAT][NBW], bfr[TBW];
 #pragma unroll
       for (int m = 0; m < NMAT; ++m)
@@ -328,12 +345,41 @@ __global__ __launch_bounds__(64 * WM * WN) void k_grouped_gemm_bf16(GemmArgs arg
             acc[m][nb][tb] =
                 __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[m][nb], bfr[tb], acc[m][nb][tb], 0, 0, 0);
     }
+  };
+
+  // Full 64-wide stages 0..nkf-1 run through one pipelined loop: stage s
+  // lives in register slot s % P.  Iteration k issues the loads of stage k+P
+  // (clamped to the last stage) into the slot stage k used, computes stage k
+  // from LDS buffer k&1, moves stage k+1 from registers into LDS buffer
+  // (k+1)&1, then one barrier.  The loop runs a multiple of P iterations; the
+  // extra ones skip the compute (uniform branch) and store data nobody reads.
+  using two = std::integral_constant<int, 2>;
+  using one = std::integral_constant<int, 1>;
+  const int nkf = K / KT;
+  if (nkf > 0) {
+#pragma unroll
+    for (int q = 0; q < P; ++q) gload(xr[q], wr[q], sr[q], min(q, nkf - 1), false);
+    lstore(xr[0], wr[0], sr[0], 0);
     __syncthreads();
-    if (kt + 1 < nk) {
-      lstore();
-      __syncthreads();
+    const int niter = (nkf + P - 1) / P * P;
+    for (int kt = 0; kt < niter; kt += P) {
+#pragma unroll
+      for (int q = 0; q < P; ++q) {
+        const int k = kt + q;
+        gload(xr[q], wr[q], sr[q], min(k + P, nkf - 1), false);
+        if (k < nkf) compute(k & 1, two{});
+        lstore(xr[(q + 1) % P], wr[(q + 1) % P], sr[(q + 1) % P], (k + 1) & 1);
+        __syncthreads();
+      }
     }
   }
+  // Trailing k-step: the last 32 of K when K % 64 == 32, and a step over zero
+  // operands otherwise.  Running it unconditionally keeps one chain for every
+  // tile variant (a zero step leaves every nonzero accumulator unchanged).
+  gload(xr[0], wr[0], sr[0], nkf, true);
+  lstore(xr[0], wr[0], sr[0], nkf & 1);
+  __syncthreads();
+  compute(nkf & 1, one{});
 
   // epilogue: lane holds features n = base + 4*(lane/16) + i (i = 0..3) of
   // token row base + lane%16 -> one 8-byte store of 4 bf16.
@@ -366,8 +412,9 @@ __global__ __launch_bounds__(256) void k_grouped_gemm_f32(GemmArgs args) {
   __shared__ float As[BM][KC + 1];
   __shared__ float Bs[NMAT][BN][KC + 1];
   __shared__ int64_t sprefix[MAXG + 1];
+  __shared__ int64_t runsum[256];
   TileInfo ti;
-  if (!find_tile<256>(args, BM, BN, blockIdx.x, ti, sprefix)) return;
+  if (!find_tile<256>(args, BM, BN, blockIdx.x, ti, sprefix, runsum)) return;
   const GemmSeg& s = args.seg[ti.seg];
   const int K = s.K, N = s.N;
   const int tid = threadIdx.x;
@@ -413,19 +460,90 @@ static int64_t seg_tile_bound(const GemmSeg& s, int BM, int BN) {
   return ((R + BM - 1) / BM + nonempty) * nt;
 }
 
-template <int BM, int BN, int WM, int WN>
-static hipError_t launch_bf16_cfg(const GemmArgs& a, bool gated, hipStream_t st) {
+template <int BM, int BN, int WM, int WN, int P, bool FP4>
+static hipError_t launch_one(const GemmArgs& a, bool gated, hipStream_t st) {
   int64_t tiles = 0;
   for (int i = 0; i < a.nseg; ++i) tiles += seg_tile_bound(a.seg[i], BM, BN);
   if (tiles == 0) return hipSuccess;
   const int64_t grid = (tiles + 7) / 8 * 8;
   if (gated)
-    hipLaunchKernelGGL((k_grouped_gemm_bf16<BM, BN, WM, WN, true>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((k_grouped_gemm_bf16<BM, BN, WM, WN, P, true, FP4>), dim3((unsigned)grid),
                        dim3(64 * WM * WN), 0, st, a);
   else
-    hipLaunchKernelGGL((k_grouped_gemm_bf16<BM, BN, WM, WN, false>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((k_grouped_gemm_bf16<BM, BN, WM, WN, P, false, FP4>), dim3((unsigned)grid),
                        dim3(64 * WM * WN), 0, st, a);
   return hipGetLastError();
+}
+
+// Segments with the same weight format share one launch; a mixed pair (MXFP4
+// routed experts + bf16 shared expert) takes one launch per format.
+template <int BM, int BN, int WM, int WN, int P>
+static hipError_t launch_bf16_cfg(const GemmArgs& a, bool gated, hipStream_t st) {
+  if (a.nseg == 1 || a.seg[0].wfmt == a.seg[1].wfmt) {
+    return a.seg[0].wfmt ? launch_one<BM, BN, WM, WN, P, true>(a, gated, st)
+                         : launch_one<BM, BN, WM, WN, P, false>(a, gated, st);
+  }
+  for (int i = 0; i < 2; ++i) {
+    GemmArgs one{};
+    one.seg[0] = a.seg[i];
+    one.nseg = 1;
+    hipError_t e = one.seg[0].wfmt ? launch_one<BM, BN, WM, WN, P, true>(one, gated, st)
+                                   : launch_one<BM, BN, WM, WN, P, false>(one, gated, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// Tile configurations (BM token rows, BN features, WM x WN waves, P stages in
+// flight).  Every configuration computes identical bits (same MFMA chain per
+// output element); they differ in occupancy, workgroup count and reuse.
+enum TileCfg {
+  TILE_16x16_1x1 = 0,   // one wave: decode, many small workgroups
+  TILE_16x32_1x2,
+  TILE_16x64_1x4,
+  TILE_32x64_1x4,
+  TILE_64x64_1x4,
+  TILE_64x64_4x1,
+  TILE_64x64_2x2,
+  TILE_128x64_4x1,
+  TILE_128x64_2x2,
+  TILE_64x32_4x1,
+  TILE_128x32_4x1,
+  TILE_32x32_2x1,
+  TILE_64x32_2x2,
+  TILE_64x64_4x1_P2,
+  TILE_32x64_2x2,
+  TILE_COUNT
+};
+
+static hipError_t launch_tile_cfg(int cfg, const GemmArgs& a, bool gated, hipStream_t st) {
+  switch (cfg) {
+    case TILE_16x16_1x1: return launch_bf16_cfg<16, 16, 1, 1, 4>(a, gated, st);
+    case TILE_16x32_1x2: return launch_bf16_cfg<16, 32, 1, 2, 4>(a, gated, st);
+    case TILE_16x64_1x4: return launch_bf16_cfg<16, 64, 1, 4, 4>(a, gated, st);
+    case TILE_32x64_1x4: return launch_bf16_cfg<32, 64, 1, 4, 4>(a, gated, st);
+    case TILE_64x64_1x4: return launch_bf16_cfg<64, 64, 1, 4, 4>(a, gated, st);
+    case TILE_64x64_4x1: return launch_bf16_cfg<64, 64, 4, 1, 4>(a, gated, st);
+    case TILE_64x64_2x2: return launch_bf16_cfg<64, 64, 2, 2, 4>(a, gated, st);
+    case TILE_128x64_4x1: return launch_bf16_cfg<128, 64, 4, 1, 3>(a, gated, st);
+    case TILE_128x64_2x2: return launch_bf16_cfg<128, 64, 2, 2, 3>(a, gated, st);
+    case TILE_64x32_4x1: return launch_bf16_cfg<64, 32, 4, 1, 4>(a, gated, st);
+    case TILE_128x32_4x1: return launch_bf16_cfg<128, 32, 4, 1, 4>(a, gated, st);
+    case TILE_32x32_2x1: return launch_bf16_cfg<32, 32, 2, 1, 4>(a, gated, st);
+    case TILE_64x32_2x2: return launch_bf16_cfg<64, 32, 2, 2, 4>(a, gated, st);
+    case TILE_64x64_4x1_P2: return launch_bf16_cfg<64, 64, 4, 1, 2>(a, gated, st);
+    default: return launch_bf16_cfg<32, 64, 2, 2, 4>(a, gated, st);
+  }
+}
+
+// Host-side choice from the average rows per group (no device sync), from
+// measured sweeps on MI355X (all choices give identical bits).
+static int pick_tile_cfg(const GemmArgs& a, bool gated, int64_t rows_per_group_hint) {
+  (void)a;
+  if (rows_per_group_hint <= 2) return gated ? TILE_16x32_1x2 : TILE_16x64_1x4;
+  if (rows_per_group_hint <= 16) return TILE_32x64_1x4;
+  if (rows_per_group_hint <= 96) return gated ? TILE_64x32_4x1 : TILE_64x64_4x1;
+  return gated ? TILE_128x64_2x2 : TILE_128x64_4x1;
 }
 
 hipError_t launch_grouped_gemm(const GemmArgs& a, bool gated, int act, int64_t rows_per_group_hint,
@@ -441,11 +559,7 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, bool gated, int act, int64_t r
       hipLaunchKernelGGL(k_grouped_gemm_f32<false>, dim3((unsigned)grid), dim3(256), 0, st, a);
     return hipGetLastError();
   }
-  // Tile shape from the average rows per group (host-side, no sync).  Every
-  // variant computes identical bits (same MFMA chain per element).
-  if (rows_per_group_hint <= 16) return launch_bf16_cfg<16, 64, 1, 4>(a, gated, st);
-  if (rows_per_group_hint <= 64) return launch_bf16_cfg<64, 64, 4, 1>(a, gated, st);
-  return launch_bf16_cfg<128, 64, 4, 1>(a, gated, st);
+  return launch_tile_cfg(pick_tile_cfg(a, gated, rows_per_group_hint), a, gated, st);
 }
 
 }  // namespace moe

@@ -30,8 +30,9 @@ struct GemmArgs {
   int nseg;
 };
 
+// zero_mask (optional): E * ceil(T/64) words cleared for launch_topk's mask.
 hipError_t launch_router_logits(const void* x, int act, const void* w, int64_t T, int D, int E,
-                                float* logits, hipStream_t s);
+                                float* logits, uint64_t* zero_mask, hipStream_t s);
 hipError_t launch_topk(const float* logits, const float* bias, int64_t T, int E, int k, int mode,
                        int32_t* idx, float* w, uint64_t* mask, hipStream_t s);
 hipError_t launch_hash_route(const int32_t* token_ids, int64_t T, int E, int k, int32_t* idx,

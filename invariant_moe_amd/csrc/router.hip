@@ -81,7 +81,15 @@ struct ActIO<float> {
 template <typename ACT, int TT, int EW>
 __global__ __launch_bounds__(256) void k_router_logits(const ACT* __restrict__ x,
                                                        const ACT* __restrict__ w, int64_t T,
-                                                       int D, int E, float* __restrict__ logits) {
+                                                       int D, int E, float* __restrict__ logits,
+                                                       unsigned long long* __restrict__ zero_words,
+                                                       int64_t n_zero) {
+  // clear the (expert, token-block) words the top-k kernel ORs into
+  if (zero_words) {
+    const int64_t nb = (int64_t)gridDim.x * gridDim.y;
+    const int64_t b = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+    for (int64_t i = b * 256 + threadIdx.x; i < n_zero; i += nb * 256) zero_words[i] = 0ull;
+  }
   constexpr int NP = TT * EW;  // pairs per wave
   constexpr int XS_BYTES = TT * 512 * (int)sizeof(ACT);
   constexpr int RED_BYTES = 4 * 32 * 64 * 4;
@@ -176,13 +184,15 @@ __global__ __launch_bounds__(256) void k_router_logits(const ACT* __restrict__ x
 }
 
 // ---------------------------------------------------------------------------
-// Top-k over one token per wave.  Selection key order: larger key first, then
-// lower expert id; keys are compared as floats (+0 == -0).  A NaN key is
-// treated as -inf so the selection stays a total order (inputs are required
-// to be finite; this only keeps the kernel memory-safe).
-// With MASK, the workgroup handles one 64-token block and also writes, for
-// every expert e, the 64-bit word of the block's tokens that selected e
-// (bit t%64), which the permutation kernel consumes.
+// Top-k, one wave per token, C = ceil(E/64) expert slots per lane.  Selection
+// key order: larger key first, then lower expert id; keys are compared as
+// floats (+0 == -0).  A NaN key is treated as -inf so the selection stays a
+// total order (inputs are required to be finite; this only keeps the kernel
+// memory-safe).  k rounds of a 64-lane butterfly arg-max; lane r keeps the
+// rank-r winner.  The weights' normaliser sums the selected terms in ascending
+// expert id.  With a mask, each selected (token, expert) sets bit t%64 of
+// word mask[e][t/64] (integer OR: order-free; the words were zeroed by the
+// logits kernel).
 // ---------------------------------------------------------------------------
 struct Cand {
   float key;
@@ -195,99 +205,78 @@ __device__ __forceinline__ bool cand_better(const Cand& a, const Cand& b) {
   return a.key > b.key || (a.key == b.key && a.id < b.id);
 }
 
-template <bool MASK>
+template <int C>
 __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits,
                                               const float* __restrict__ bias, int64_t T, int E,
                                               int k, int mode, int32_t* __restrict__ topk_idx,
                                               float* __restrict__ topk_w,
-                                              uint64_t* __restrict__ mask, int64_t W) {
-  __shared__ unsigned long long smask[MOE_MAX_EXPERTS];
-  __shared__ int s_id[4][MOE_MAX_TOPK];
-  __shared__ float s_val[4][MOE_MAX_TOPK];
-  __shared__ float s_z[4][MOE_MAX_TOPK];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t tb = blockIdx.x;
-  if (MASK) {
-    for (int e = threadIdx.x; e < E; e += 256) smask[e] = 0ull;
-    __syncthreads();
+                                              unsigned long long* __restrict__ mask, int64_t W) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;  // whole wave; no workgroup barriers below
+  float key[C], val[C];
+  uint32_t taken = 0;
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int e = lane + 64 * c;
+    key[c] = 0.0f;
+    val[c] = 0.0f;
+    if (e < E) {
+      const float l = logits[t * E + e];
+      const float sc = (mode == MOE_ROUTE_SIGMOID) ? routing_sigmoid(l) : l;
+      float kk = bias ? sc + bias[e] : sc;
+      if (kk != kk) kk = -__builtin_inff();
+      key[c] = kk;
+      val[c] = sc;
+    } else {
+      taken |= 1u << c;
+    }
   }
-  constexpr int C = MOE_MAX_EXPERTS / 64;
-  // 16 passes of 4 tokens (one per wave); every wave runs every pass so the
-  // workgroup barriers below are uniform.
-  for (int pass = 0; pass < 16; ++pass) {
-    const int tt = pass * 4 + wave;
-    const int64_t t = tb * 64 + tt;
-    const bool valid = t < T;  // uniform per wave
-    if (valid) {
-      float key[C], val[C];
-      uint32_t taken = 0;
+  int my_id = 0;
+  float my_val = 0.0f;
+  for (int r = 0; r < k; ++r) {
+    Cand best{0.0f, -1};
 #pragma unroll
-      for (int c = 0; c < C; ++c) {
-        const int e = lane + 64 * c;
-        key[c] = 0.0f;
-        val[c] = 0.0f;
-        if (e < E) {
-          const float l = logits[t * E + e];
-          const float s = (mode == MOE_ROUTE_SIGMOID) ? routing_sigmoid(l) : l;
-          float kk = bias ? s + bias[e] : s;
-          if (kk != kk) kk = -__builtin_inff();
-          key[c] = kk;
-          val[c] = s;
-        } else {
-          taken |= 1u << c;
-        }
-      }
-      for (int r = 0; r < k; ++r) {
-        Cand best{0.0f, -1};
-#pragma unroll
-        for (int c = 0; c < C; ++c) {
-          Cand cc{key[c], ((taken >> c) & 1u) ? -1 : lane + 64 * c};
-          if (cand_better(cc, best)) best = cc;
-        }
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) {
-          Cand o{__shfl_xor(best.key, m), __shfl_xor(best.id, m)};
-          if (cand_better(o, best)) best = o;
-        }
-        // best.id >= 0 because k <= E; its owner lane records it.
-        if (best.id >= 0 && (best.id & 63) == lane) {
-          const int c = best.id >> 6;
-          taken |= 1u << c;
-          float v = 0.0f;
-#pragma unroll
-          for (int cc = 0; cc < C; ++cc)
-            if (cc == c) v = val[cc];
-          s_id[wave][r] = best.id;
-          s_val[wave][r] = v;
-        }
-      }
+    for (int c = 0; c < C; ++c) {
+      Cand cc{key[c], ((taken >> c) & 1u) ? -1 : lane + 64 * c};
+      if (cand_better(cc, best)) best = cc;
     }
-    __syncthreads();
-    // weights: z_r = exp(l_r - l_top) (softmax) or s_r (sigmoid); Z sums the
-    // z in ascending expert id, from +0, in fp32.
-    float z = 0.0f;
-    int id = 0;
-    if (valid && lane < k) {
-      id = s_id[wave][lane];
-      z = (mode == MOE_ROUTE_SOFTMAX) ? routing_exp(s_val[wave][lane] - s_val[wave][0])
-                                      : s_val[wave][lane];
-      int pos = 0;
-      for (int q = 0; q < k; ++q) pos += (s_id[wave][q] < id) ? 1 : 0;
-      s_z[wave][pos] = z;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      Cand o{__shfl_xor(best.key, m), __shfl_xor(best.id, m)};
+      if (cand_better(o, best)) best = o;
     }
-    __syncthreads();
-    if (valid && lane < k) {
-      float Z = 0.0f;
-      for (int q = 0; q < k; ++q) Z = Z + s_z[wave][q];
-      topk_idx[t * k + lane] = id;
-      topk_w[t * k + lane] = z / Z;
-      if (MASK) atomicOr(&smask[id], 1ull << (tt & 63));
+    const int win = best.id < 0 ? 0 : best.id;  // k <= E: always a winner
+    const int owner = win & 63;
+    float ov = 0.0f;
+    if (lane == owner) {
+      taken |= 1u << (win >> 6);
+#pragma unroll
+      for (int c = 0; c < C; ++c)
+        if (c == (win >> 6)) ov = val[c];
     }
-    __syncthreads();
+    ov = __shfl(ov, owner);
+    if (lane == r) {
+      my_id = win;
+      my_val = ov;
+    }
   }
-  if (MASK) {
-    __syncthreads();
-    for (int e = threadIdx.x; e < E; e += 256) mask[(int64_t)e * W + tb] = smask[e];
+  const float top = __shfl(my_val, 0);
+  const bool act = lane < k;
+  const float z = !act ? 0.0f
+                       : (mode == MOE_ROUTE_SOFTMAX ? routing_exp(my_val - top) : my_val);
+  int pos = 0;  // rank of this slot by ascending expert id
+  for (int q = 0; q < k; ++q) pos += (__shfl(my_id, q) < my_id) ? 1 : 0;
+  float Z = 0.0f;
+  for (int i = 0; i < k; ++i) {
+    const unsigned long long b = __ballot(act && pos == i);
+    const int src = b ? __builtin_ctzll(b) : 0;
+    Z = Z + __shfl(z, src);
+  }
+  if (act) {
+    topk_idx[t * k + lane] = my_id;
+    topk_w[t * k + lane] = z / Z;
+    if (mask) atomicOr(&mask[(int64_t)my_id * W + (t >> 6)], 1ull << (t & 63));
   }
 }
 
@@ -354,42 +343,52 @@ __global__ __launch_bounds__(256) void k_routing_scores(const float* __restrict_
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+template <int TT, int EW>
+static void launch_logits_cfg(const void* x, int act, const void* w, int64_t T, int D, int E,
+                              float* logits, unsigned long long* zw, int64_t nz, hipStream_t s) {
+  dim3 grid((unsigned)((T + TT - 1) / TT), (unsigned)((E + 4 * EW - 1) / (4 * EW)));
+  if (act == MOE_BF16)
+    hipLaunchKernelGGL((k_router_logits<uint16_t, TT, EW>), grid, dim3(256), 0, s,
+                       (const uint16_t*)x, (const uint16_t*)w, T, D, E, logits, zw, nz);
+  else
+    hipLaunchKernelGGL((k_router_logits<float, TT, EW>), grid, dim3(256), 0, s, (const float*)x,
+                       (const float*)w, T, D, E, logits, zw, nz);
+}
+
 hipError_t launch_router_logits(const void* x, int act, const void* w, int64_t T, int D, int E,
-                                float* logits, hipStream_t s) {
+                                float* logits, uint64_t* zero_mask, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  // Small batches: one (token, expert-quad) per workgroup keeps many
-  // workgroups streaming the router weights; large batches reuse each loaded
-  // router row for 16 tokens.  Both give identical logits.
-  if (T <= 32) {
-    dim3 grid((unsigned)T, (unsigned)((E + 3) / 4));
-    if (act == MOE_BF16)
-      hipLaunchKernelGGL((k_router_logits<uint16_t, 1, 1>), grid, dim3(256), 0, s,
-                         (const uint16_t*)x, (const uint16_t*)w, T, D, E, logits);
-    else
-      hipLaunchKernelGGL((k_router_logits<float, 1, 1>), grid, dim3(256), 0, s,
-                         (const float*)x, (const float*)w, T, D, E, logits);
-  } else {
-    dim3 grid((unsigned)((T + 15) / 16), (unsigned)((E + 31) / 32));
-    if (act == MOE_BF16)
-      hipLaunchKernelGGL((k_router_logits<uint16_t, 16, 8>), grid, dim3(256), 0, s,
-                         (const uint16_t*)x, (const uint16_t*)w, T, D, E, logits);
-    else
-      hipLaunchKernelGGL((k_router_logits<float, 16, 8>), grid, dim3(256), 0, s,
-                         (const float*)x, (const float*)w, T, D, E, logits);
-  }
+  unsigned long long* zw = reinterpret_cast<unsigned long long*>(zero_mask);
+  const int64_t nz = zero_mask ? (int64_t)E * ((T + 63) / 64) : 0;
+  // Tile choice only changes how many (token, expert) pairs a workgroup holds
+  // (enough workgroups to stream the router weights); every pair's logit is
+  // the same fixed chain.
+  if (((T + 15) / 16) * ((E + 31) / 32) >= 512)
+    launch_logits_cfg<16, 8>(x, act, w, T, D, E, logits, zw, nz, s);
+  else if (T >= 8)
+    launch_logits_cfg<4, 2>(x, act, w, T, D, E, logits, zw, nz, s);
+  else
+    launch_logits_cfg<1, 1>(x, act, w, T, D, E, logits, zw, nz, s);
   return hipGetLastError();
+}
+
+template <int C>
+static void launch_topk_cfg(const float* logits, const float* bias, int64_t T, int E, int k,
+                            int mode, int32_t* idx, float* w, uint64_t* mask, hipStream_t s) {
+  const int64_t W = (T + 63) / 64;
+  hipLaunchKernelGGL(k_topk<C>, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, logits, bias, T,
+                     E, k, mode, idx, w, reinterpret_cast<unsigned long long*>(mask), W);
 }
 
 hipError_t launch_topk(const float* logits, const float* bias, int64_t T, int E, int k, int mode,
                        int32_t* idx, float* w, uint64_t* mask, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  const int64_t W = (T + 63) / 64;
-  if (mask)
-    hipLaunchKernelGGL(k_topk<true>, dim3((unsigned)W), dim3(256), 0, s, logits, bias, T, E, k,
-                       mode, idx, w, mask, W);
-  else
-    hipLaunchKernelGGL(k_topk<false>, dim3((unsigned)W), dim3(256), 0, s, logits, bias, T, E, k,
-                       mode, idx, w, (uint64_t*)nullptr, W);
+  const int c = (E + 63) / 64;
+  if (c <= 1) launch_topk_cfg<1>(logits, bias, T, E, k, mode, idx, w, mask, s);
+  else if (c <= 2) launch_topk_cfg<2>(logits, bias, T, E, k, mode, idx, w, mask, s);
+  else if (c <= 4) launch_topk_cfg<4>(logits, bias, T, E, k, mode, idx, w, mask, s);
+  else if (c <= 8) launch_topk_cfg<8>(logits, bias, T, E, k, mode, idx, w, mask, s);
+  else launch_topk_cfg<16>(logits, bias, T, E, k, mode, idx, w, mask, s);
   return hipGetLastError();
 }
 
