@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOPK 32
 
@@ -176,9 +176,11 @@ int moe_permute(const int32_t* topk_idx, int64_t T, int k, int E, int32_t* exper
  * other rows and of their number.
  *  R: number of rows (= expert_offsets[E]); for a shared expert pass E = 1 and
  *  expert_offsets = {0, T}.  flags: must be 0 (reserved).
- *  workspace: moe_grouped_swiglu_workspace_bytes(R, I, act) bytes (h).
+ *  row_index entries must be valid rows of x_rows (they are not checked).
+ *  workspace: moe_grouped_swiglu_workspace_bytes(R, E, D, I, act) bytes
+ *  (h rows, and the tile tables that the call writes from expert_offsets).
  * ------------------------------------------------------------------------- */
-size_t moe_grouped_swiglu_workspace_bytes(int64_t R, int I, moe_dtype act);
+size_t moe_grouped_swiglu_workspace_bytes(int64_t R, int E, int D, int I, moe_dtype act);
 int moe_grouped_swiglu(const void* x_rows, const int32_t* row_index,
                        const int32_t* expert_offsets, int64_t R, int E, int D, int I,
                        const moe_expert_weights* w, moe_dtype act, uint32_t flags, void* out,

@@ -56,7 +56,7 @@ def lib() -> ctypes.CDLL:
         L.moe_permute_workspace_bytes.argtypes = [i64, i32]
         L.moe_permute_workspace_bytes.restype = sz
         L.moe_permute.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp, vp, i32, i32, vp, vp, sz, vp]
-        L.moe_grouped_swiglu_workspace_bytes.argtypes = [i64, i32, i32]
+        L.moe_grouped_swiglu_workspace_bytes.argtypes = [i64, i32, i32, i32, i32]
         L.moe_grouped_swiglu_workspace_bytes.restype = sz
         L.moe_grouped_swiglu.argtypes = [vp, vp, vp, i64, i32, i32, i32, WP, i32, u32, vp, vp, sz, vp]
         L.moe_combine.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i32, vp, vp]
@@ -192,7 +192,7 @@ def grouped_swiglu(x_rows, row_index, expert_offsets, R: int, E: int, weights: E
     if out is None:
         out = torch.empty((R, D), dtype=x_rows.dtype, device=x_rows.device)
     L = lib()
-    nb = L.moe_grouped_swiglu_workspace_bytes(R, I, act)
+    nb = L.moe_grouped_swiglu_workspace_bytes(R, E, D, I, act)
     ws = _workspace(nb, x_rows.device)
     wst = weights.as_struct()
     _check(L.moe_grouped_swiglu(_ptr(x_rows), _ptr(row_index), _ptr(expert_offsets), R, E, D, I,

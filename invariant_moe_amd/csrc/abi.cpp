@@ -51,8 +51,43 @@ struct Carver {
   }
 };
 
+// The two grouped GEMMs of the expert FFN (gate/up, then down) as the host
+// planner sees them: routed experts grouped by the device offsets, plus the
+// shared expert as one group of T rows.
+struct FfnPlans {
+  moe::GemmPlan up, dn;
+};
+
+FfnPlans ffn_plans(int64_t R, int64_t T, int D, int E, int I, int Is, moe_dtype act,
+                   int routed_wfmt, int shared_wfmt) {
+  const int64_t hint = R / E;
+  moe::SegShape su[2] = {{true, R, E, D, I, routed_wfmt}, {false, T, 1, D, Is, shared_wfmt}};
+  moe::SegShape sd[2] = {{true, R, E, I, D, routed_wfmt}, {false, T, 1, Is, D, shared_wfmt}};
+  const int nseg = Is > 0 ? 2 : 1;
+  FfnPlans p;
+  p.up = moe::plan_grouped_gemm(su, nseg, true, act, hint);
+  p.dn = moe::plan_grouped_gemm(sd, nseg, false, act, hint);
+  return p;
+}
+
+// Tile-table entries reserved for a layer: the larger of the one-launch and
+// the per-format (two-launch) plans, so the size does not depend on the
+// weight formats.
+int64_t layer_table_entries(int64_t T, int D, int E, int k, int I, int Is, moe_dtype act) {
+  const int64_t R = T * k;
+  int64_t n = 0;
+  for (int split = 0; split < 2; ++split) {
+    const FfnPlans p = ffn_plans(R, T, D, E, I, Is, act, 0, split);
+    const int64_t m = moe::plan_table_entries(p.up) + moe::plan_table_entries(p.dn);
+    n = m > n ? m : n;
+  }
+  return n;
+}
+
 struct LayerLayout {
-  size_t logits, idx, w, mask, wprefix, counts, offsets, row_token, pair_row, h, hs, o, s, total;
+  size_t logits, idx, w, mask, wprefix, counts, offsets, row_token, pair_row, h, hs, o, s, tiles,
+      total;
+  int64_t tile_entries;
 };
 
 LayerLayout layer_layout(int64_t T, int D, int E, int k, int I, int Is, moe_dtype act) {
@@ -73,6 +108,8 @@ LayerLayout layer_layout(int64_t T, int D, int E, int k, int I, int Is, moe_dtyp
   L.hs = c.take((size_t)T * (Is > 0 ? Is : 0) * es);
   L.o = c.take((size_t)R * D * es);
   L.s = c.take((size_t)T * (Is > 0 ? D : 0) * es);
+  L.tile_entries = layer_table_entries(T, D, E, k, I, Is, act);
+  L.tiles = c.take((size_t)L.tile_entries * sizeof(int4));
   L.total = c.off;
   return L;
 }
@@ -251,15 +288,21 @@ int moe_permute(const int32_t* topk_idx, int64_t T, int k, int E, int32_t* exper
   hipError_t e = moe::launch_mask_from_idx(topk_idx, T, k, E, mask, s);
   if (e == hipSuccess)
     e = moe::launch_permute(topk_idx, T, k, E, mask, wprefix, expert_counts, expert_offsets,
-                            row_token, pair_row, s);
+                            row_token, pair_row, nullptr, s);
   if (e == hipSuccess && x)
     e = moe::launch_gather_rows(x, row_token, T, T * k, (int64_t)D * act_size(act), x_perm, s);
   return hip_status(e, "permute");
 }
 
-size_t moe_grouped_swiglu_workspace_bytes(int64_t R, int I, moe_dtype act) {
-  if (R <= 0 || I <= 0) return 0;
-  return align_up((size_t)R * I * act_size(act == MOE_F32 ? MOE_F32 : MOE_BF16));
+// h rows, then the tile tables of the two GEMMs.
+size_t moe_grouped_swiglu_workspace_bytes(int64_t R, int E, int D, int I, moe_dtype act) {
+  if (R <= 0 || E <= 0 || D <= 0 || I <= 0) return 0;
+  const moe_dtype a = act == MOE_F32 ? MOE_F32 : MOE_BF16;
+  const FfnPlans p = ffn_plans(R, 0, D, E, I, 0, a, 0, 0);
+  Carver c;
+  c.take((size_t)R * I * act_size(a));
+  c.take((size_t)(moe::plan_table_entries(p.up) + moe::plan_table_entries(p.dn)) * sizeof(int4));
+  return c.off;
 }
 
 int moe_grouped_swiglu(const void* x_rows, const int32_t* row_index, const int32_t* expert_offsets,
@@ -276,22 +319,31 @@ int moe_grouped_swiglu(const void* x_rows, const int32_t* row_index, const int32
   if ((rc = check_weights(w, act, "expert"))) return rc;
   if (!expert_offsets || !out || (R > 0 && !x_rows)) return fail(MOE_ERR_NULL, "NULL argument");
   if ((x_rows && !aligned(x_rows, 16)) || !aligned(out, 16)) return fail(MOE_ERR_ALIGN, "x_rows / out misaligned");
-  const size_t need = moe_grouped_swiglu_workspace_bytes(R, I, act);
+  const size_t need = moe_grouped_swiglu_workspace_bytes(R, E, D, I, act);
   if (need && (!workspace || workspace_bytes < need))
     return fail(MOE_ERR_WORKSPACE, "grouped_swiglu workspace needs %zu bytes", need);
   if (workspace && !aligned(workspace, 16)) return fail(MOE_ERR_ALIGN, "workspace misaligned");
   if (R == 0) return ok();
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t hint = R / E;
+  const FfnPlans p = ffn_plans(R, 0, D, E, I, 0, act, w->dtype == MOE_MXFP4 ? 1 : 0, 0);
+  if (!p.up.valid || !p.dn.valid) return fail(MOE_ERR_SHAPE, "problem too large for one launch");
+  Carver c;
+  c.take((size_t)R * I * act_size(act));
+  int4* tiles_up = reinterpret_cast<int4*>(static_cast<char*>(workspace) + c.off);
+  int4* tiles_dn = tiles_up + moe::plan_table_entries(p.up);
+  moe::TileJobs jobs{};
+  if (!moe::plan_tile_jobs(p.up, tiles_up, jobs) || !moe::plan_tile_jobs(p.dn, tiles_dn, jobs))
+    return fail(MOE_ERR_UNSUPPORTED, "gate/up and down GEMM plans use different row tiles");
+  hipError_t e = moe::launch_tile_tables(expert_offsets, E, jobs, s);
   moe::GemmArgs up{};
   up.nseg = 1;
   up.seg[0] = make_seg(x_rows, row_index, expert_offsets, R, E, D, I, w, true, workspace);
-  hipError_t e = moe::launch_grouped_gemm(up, true, act, hint, s);
+  if (e == hipSuccess) e = moe::launch_grouped_gemm(p.up, up, tiles_up, s);
   if (e == hipSuccess) {
     moe::GemmArgs dn{};
     dn.nseg = 1;
     dn.seg[0] = make_seg(workspace, nullptr, expert_offsets, R, E, I, D, w, false, out);
-    e = moe::launch_grouped_gemm(dn, false, act, hint, s);
+    e = moe::launch_grouped_gemm(p.dn, dn, tiles_dn, s);
   }
   return hip_status(e, "grouped_swiglu");
 }
@@ -382,11 +434,21 @@ int moe_layer_forward(const void* x, const int32_t* token_ids, const void* w_rou
   }
   if (e != hipSuccess) return hip_status(e, "routing");
   record_stage(1, s);
-  e = moe::launch_permute(idx, T, k, E, mask, wprefix, counts, offsets, row_token, pair_row, s);
+  const FfnPlans p = ffn_plans(R, T, D, E, I, Is, act, routed->dtype == MOE_MXFP4 ? 1 : 0,
+                               shared && shared->dtype == MOE_MXFP4 ? 1 : 0);
+  if (!p.up.valid || !p.dn.valid) return fail(MOE_ERR_SHAPE, "problem too large for one launch");
+  if (moe::plan_table_entries(p.up) + moe::plan_table_entries(p.dn) > L.tile_entries)
+    return fail(MOE_ERR_WORKSPACE, "tile tables exceed their workspace region");
+  int4* tiles_up = reinterpret_cast<int4*>(ws + L.tiles);
+  int4* tiles_dn = tiles_up + moe::plan_table_entries(p.up);
+  moe::TileJobs jobs{};
+  if (!moe::plan_tile_jobs(p.up, tiles_up, jobs) || !moe::plan_tile_jobs(p.dn, tiles_dn, jobs))
+    return fail(MOE_ERR_UNSUPPORTED, "gate/up and down GEMM plans use different row tiles");
+  e = moe::launch_permute(idx, T, k, E, mask, wprefix, counts, offsets, row_token, pair_row, &jobs,
+                          s);
   if (e != hipSuccess) return hip_status(e, "permute");
   record_stage(2, s);
 
-  const int64_t hint = R / E;
   moe::GemmArgs up{};
   up.seg[0] = make_seg(x, row_token, offsets, R, E, D, I, routed, true, h);
   up.nseg = 1;
@@ -394,7 +456,7 @@ int moe_layer_forward(const void* x, const int32_t* token_ids, const void* w_rou
     up.seg[1] = make_seg(x, nullptr, nullptr, T, 1, D, Is, shared, true, hs);
     up.nseg = 2;
   }
-  e = moe::launch_grouped_gemm(up, true, act, hint, s);
+  e = moe::launch_grouped_gemm(p.up, up, tiles_up, s);
   if (e != hipSuccess) return hip_status(e, "gate/up GEMM");
   record_stage(3, s);
 
@@ -405,7 +467,7 @@ int moe_layer_forward(const void* x, const int32_t* token_ids, const void* w_rou
     dn.seg[1] = make_seg(hs, nullptr, nullptr, T, 1, Is, D, shared, false, sh);
     dn.nseg = 2;
   }
-  e = moe::launch_grouped_gemm(dn, false, act, hint, s);
+  e = moe::launch_grouped_gemm(p.dn, dn, tiles_dn, s);
   if (e != hipSuccess) return hip_status(e, "down GEMM");
   record_stage(4, s);
 

@@ -24,18 +24,18 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "tiles.hpp"
 
 namespace moe {
 
 constexpr int KT = 64;         // K per LDS stage (two MFMA k-steps)
 constexpr int LDK = KT + 8;    // padded LDS row (bf16 elements) -> 144 B stride
-constexpr int MAXG = MOE_MAX_EXPERTS + 1;
 
 // ---------------------------------------------------------------------------
-// Work list: the tiles of all groups of both segments, group-major, then
-// n-tile, then m-tile (m fastest, so neighbouring tiles share weight panels).
-// Every workgroup computes the prefix of tile counts itself from the device
-// row offsets (no host sync, no extra launch).
+// Work list: one tile descriptor per workgroup, written on the device from the
+// group offsets before the launch (tile order and XCD placement: tiles.hpp).
+// A descriptor that does not fit its segment is treated as "no tile", so no
+// access leaves the row, weight or output ranges whatever the table holds.
 // ---------------------------------------------------------------------------
 struct TileInfo {
   int seg, g;
@@ -44,76 +44,17 @@ struct TileInfo {
   int n0;        // first output feature
 };
 
-// Rows of group g; offsets outside [0, M] or decreasing (outside the
-// contract) give an empty group so no access leaves the row range.
-__device__ __forceinline__ int64_t group_rows(const GemmSeg& s, int g) {
-  if (!s.offsets) return s.M;
-  const int64_t a = s.offsets[g], b = s.offsets[g + 1];
-  return (a < 0 || b > s.M || b < a) ? 0 : b - a;
-}
-
-template <int NT>
-__device__ bool find_tile(const GemmArgs& a, int BM, int BN, int64_t bid, TileInfo& ti,
-                          int64_t* sprefix /* [MAXG + 1] */, int64_t* runsum /* [NT] */) {
-  const int G0 = a.seg[0].G;
-  const int Gt = G0 + (a.nseg > 1 ? a.seg[1].G : 0);
-  // per-group tile counts
-  for (int g = threadIdx.x; g < Gt; g += NT) {
-    const GemmSeg& s = (g < G0) ? a.seg[0] : a.seg[1];
-    const int gl = (g < G0) ? g : g - G0;
-    const int64_t M = group_rows(s, gl);
-    const int64_t mt = (M + BM - 1) / BM;
-    const int64_t nt = (s.N + BN - 1) / BN;
-    sprefix[g] = mt * nt;
-  }
-  __syncthreads();
-  // exclusive scan (Gt <= 1025): each thread owns a contiguous run; run sums
-  // are scanned with wave shuffles, then across the NT/64 waves.
-  const int per = (Gt + NT - 1) / NT;
-  const int beg = threadIdx.x * per;
-  const int end = min(beg + per, Gt);
-  int64_t loc = 0;
-  for (int g = beg; g < end; ++g) loc += sprefix[g];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int64_t incl = loc;
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    const int64_t o = __shfl_up(incl, m);
-    if (lane >= m) incl += o;
-  }
-  if (lane == 63) runsum[wave] = incl;
-  __syncthreads();
-  int64_t run = incl - loc;
-  for (int w = 0; w < wave; ++w) run += runsum[w];
-  if (threadIdx.x == NT - 1) sprefix[MAXG] = run + loc;  // total
-  for (int g = beg; g < end; ++g) {
-    const int64_t v = sprefix[g];
-    sprefix[g] = run;
-    run += v;
-  }
-  __syncthreads();
-  const int64_t total = sprefix[MAXG];
-  const int64_t l = xcd_logical_block(bid, total);
-  if (l < 0) return false;
-  // last group whose prefix <= l (binary search over a non-decreasing array)
-  int lo = 0, hi = Gt - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (sprefix[mid] <= l) lo = mid; else hi = mid - 1;
-  }
-  const int g = lo;
-  const int seg = (g < G0) ? 0 : 1;
-  const int gl = (g < G0) ? g : g - G0;
+__device__ __forceinline__ bool read_tile(const GemmArgs& a, int BM, TileInfo& ti) {
+  const int4 d = a.tiles[blockIdx.x];
+  const int seg = d.z >> 16, g = d.z & 0xffff;
+  if (d.y <= 0 || d.y > BM || d.x < 0 || seg >= a.nseg) return false;
   const GemmSeg& s = a.seg[seg];
-  const int64_t M = group_rows(s, gl);
-  const int64_t mt = (M + BM - 1) / BM;
-  const int64_t local = l - sprefix[g];
-  const int64_t ntile = local / mt, mtile = local % mt;
+  if (g >= s.G || (int64_t)d.x + d.y > s.M || d.w < 0 || d.w >= s.N) return false;
   ti.seg = seg;
-  ti.g = gl;
-  ti.row0 = (s.offsets ? (int64_t)s.offsets[gl] : 0) + mtile * BM;
-  ti.rows = (int)min((int64_t)BM, M - mtile * BM);
-  ti.n0 = (int)(ntile * BN);
+  ti.g = g;
+  ti.row0 = d.x;
+  ti.rows = d.y;
+  ti.n0 = d.w;
   return true;
 }
 
@@ -167,17 +108,10 @@ __global__ __launch_bounds__(64 * WM * WN) void k_grouped_gemm_bf16(GemmArgs arg
   constexpr int QPT = (QCH + NT - 1) / NT;
   constexpr int WQ = FP4 ? QPT : WPT;
   constexpr int BUF = (BM + NMAT * BN) * LDK;  // bf16 elements of one LDS stage
-  constexpr int TILE_BYTES = 2 * BUF * 2;
-  constexpr int PREFIX_BYTES = (MAXG + 1 + NT) * 8;
-  constexpr int SMEM = TILE_BYTES > PREFIX_BYTES ? TILE_BYTES : PREFIX_BYTES;
-  __shared__ __align__(16) unsigned char smem[SMEM];
+  __shared__ __align__(16) unsigned char smem[2 * BUF * 2];
 
   TileInfo ti;
-  {
-    int64_t* sprefix = reinterpret_cast<int64_t*>(smem);
-    if (!find_tile<NT>(args, BM, BN, blockIdx.x, ti, sprefix, sprefix + MAXG + 1)) return;
-    __syncthreads();  // the prefix area is reused for the tiles below
-  }
+  if (!read_tile(args, BM, ti)) return;
   uint16_t* lds = reinterpret_cast<uint16_t*>(smem);  // [2][BM + NMAT*BN][LDK]
   const GemmSeg& s = args.seg[ti.seg];
   const int K = s.K, N = s.N;
@@ -185,17 +119,21 @@ __global__ __launch_bounds__(64 * WM * WN) void k_grouped_gemm_bf16(GemmArgs arg
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % WM, wn = wave / WM;
 
-  // per-thread source pointers of the token tile (rows clamped into range)
-  const uint16_t* xsrc[XPT];
+  // Token rows of this thread's chunks (rows clamped into the tile).  With a
+  // row index the indices are loaded here, before the weight prefetch below,
+  // so that waiting for them does not wait for the weights.
+  int64_t xrow[XPT];
 #pragma unroll
   for (int i = 0; i < XPT; ++i) {
     const int c = tid + i * NT;
-    const int r = min(c / (KT / 8), BM - 1);
-    const int rr = min(r, ti.rows - 1);
-    const int64_t row = ti.row0 + rr;
-    const int64_t src = s.a_index ? (int64_t)s.a_index[row] : row;
-    xsrc[i] = static_cast<const uint16_t*>(s.A) + src * K + (c % (KT / 8)) * 8;
+    const int r = min(min(c / (KT / 8), BM - 1), ti.rows - 1);
+    xrow[i] = ti.row0 + r;
   }
+  if (s.a_index) {
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) xrow[i] = s.a_index[xrow[i]];
+  }
+  const uint16_t* xsrc[XPT];
   // weight tile sources
   const uint8_t* wsrc[WQ];
   const uint8_t* ssrc[QPT];
@@ -238,7 +176,6 @@ __global__ __launch_bounds__(64 * WM * WN) void k_grouped_gemm_bf16(GemmArgs arg
   uint4 xr[P][XPT];
   uint4 wr[P][WQ];
   uint32_t sr[P][QPT];
-  const int nk = (K + KT - 1) / KT;
 
   // Branch-free stage load (every lane always issues the same loads, from
   // clamped in-range addresses; out-of-tile parts are zeroed afterwards), so
@@ -248,7 +185,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_grouped_gemm_bf16(GemmArgs arg
   // address and skip the LDS store), so the compiler can wait for exactly one
   // stage while the others stay in flight.  half == true loads the first 32
   // k of the last stage when K % 64 == 32 and zeroes the rest.
-  auto gload = [&](uint4 (&xq)[XPT], uint4 (&wq)[WQ], uint32_t (&sq)[QPT], int kt, bool half) {
+  auto gload_x = [&](uint4 (&xq)[XPT], int kt, bool half) {
     const int k0 = kt * KT;
     const bool none = half && (K % KT) == 0;  // trailing step over zeros
 #pragma unroll
@@ -259,6 +196,10 @@ __global__ __launch_bounds__(64 * WM * WN) void k_grouped_gemm_bf16(GemmArgs arg
       else
         xq[i] = *reinterpret_cast<const uint4*>(xsrc[i] + k0);
     }
+  };
+  auto gload_w = [&](uint4 (&wq)[WQ], uint32_t (&sq)[QPT], int kt, bool half) {
+    const int k0 = kt * KT;
+    const bool none = half && (K % KT) == 0;
     if constexpr (!fp4) {
 #pragma unroll
       for (int i = 0; i < WPT; ++i) {
@@ -281,6 +222,10 @@ __global__ __launch_bounds__(64 * WM * WN) void k_grouped_gemm_bf16(GemmArgs arg
         }
       }
     }
+  };
+  auto gload = [&](uint4 (&xq)[XPT], uint4 (&wq)[WQ], uint32_t (&sq)[QPT], int kt, bool half) {
+    gload_x(xq, kt, half);
+    gload_w(wq, sq, kt, half);
   };
   auto lstore = [&](const uint4 (&xq)[XPT], const uint4 (&wq)[WQ], const uint32_t (&sq)[QPT],
                     int buf) {
@@ -358,7 +303,19 @@ __global__ __launch_bounds__(64 * WM * WN) void k_grouped_gemm_bf16(GemmArgs arg
   const int nkf = K / KT;
   if (nkf > 0) {
 #pragma unroll
-    for (int q = 0; q < P; ++q) gload(xr[q], wr[q], sr[q], min(q, nkf - 1), false);
+    for (int q = 0; q < P; ++q) gload_w(wr[q], sr[q], min(q, nkf - 1), false);
+  }
+  // The weight stream does not depend on the token rows: it is in flight
+  // before the row indices are consumed.
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < XPT; ++i) {
+    const int c = tid + i * NT;
+    xsrc[i] = static_cast<const uint16_t*>(s.A) + xrow[i] * K + (c % (KT / 8)) * 8;
+  }
+  if (nkf > 0) {
+#pragma unroll
+    for (int q = 0; q < P; ++q) gload_x(xr[q], min(q, nkf - 1), false);
     lstore(xr[0], wr[0], sr[0], 0);
     __syncthreads();
     const int niter = (nkf + P - 1) / P * P;
@@ -411,10 +368,8 @@ __global__ __launch_bounds__(256) void k_grouped_gemm_f32(GemmArgs args) {
   constexpr int NMAT = GATED ? 2 : 1;
   __shared__ float As[BM][KC + 1];
   __shared__ float Bs[NMAT][BN][KC + 1];
-  __shared__ int64_t sprefix[MAXG + 1];
-  __shared__ int64_t runsum[256];
   TileInfo ti;
-  if (!find_tile<256>(args, BM, BN, blockIdx.x, ti, sprefix, runsum)) return;
+  if (!read_tile(args, BM, ti)) return;
   const GemmSeg& s = args.seg[ti.seg];
   const int K = s.K, N = s.N;
   const int tid = threadIdx.x;
@@ -448,24 +403,20 @@ __global__ __launch_bounds__(256) void k_grouped_gemm_f32(GemmArgs args) {
 }
 
 // ---------------------------------------------------------------------------
-// launch: grid = an upper bound of the tile count (rounded to the 8 XCDs);
-// workgroups past the real count exit after the prefix.
+// Host planning and launch.  The grid of a launch is an upper bound of its
+// tile count known without a device sync; surplus workgroups read an empty
+// descriptor and exit.
 // ---------------------------------------------------------------------------
-static int64_t seg_tile_bound(const GemmSeg& s, int BM, int BN) {
+static int64_t seg_tile_bound(const SegShape& s, int BM, int BN) {
   const int64_t nt = (s.N + BN - 1) / BN;
-  if (!s.offsets) return ((s.M + BM - 1) / BM) * nt;
+  if (!s.grouped) return ((s.M + BM - 1) / BM) * nt;
   // sum_g ceil(M_g/BM) <= ceil(R/BM) + (number of non-empty groups)
-  const int64_t R = s.M;  // total rows of the segment
-  const int64_t nonempty = R < s.G ? R : s.G;
-  return ((R + BM - 1) / BM + nonempty) * nt;
+  const int64_t nonempty = s.M < s.G ? s.M : s.G;
+  return ((s.M + BM - 1) / BM + nonempty) * nt;
 }
 
 template <int BM, int BN, int WM, int WN, int P, bool FP4>
-static hipError_t launch_one(const GemmArgs& a, bool gated, hipStream_t st) {
-  int64_t tiles = 0;
-  for (int i = 0; i < a.nseg; ++i) tiles += seg_tile_bound(a.seg[i], BM, BN);
-  if (tiles == 0) return hipSuccess;
-  const int64_t grid = (tiles + 7) / 8 * 8;
+static hipError_t launch_one(const GemmArgs& a, bool gated, int64_t grid, hipStream_t st) {
   if (gated)
     hipLaunchKernelGGL((k_grouped_gemm_bf16<BM, BN, WM, WN, P, true, FP4>), dim3((unsigned)grid),
                        dim3(64 * WM * WN), 0, st, a);
@@ -473,25 +424,6 @@ static hipError_t launch_one(const GemmArgs& a, bool gated, hipStream_t st) {
     hipLaunchKernelGGL((k_grouped_gemm_bf16<BM, BN, WM, WN, P, false, FP4>), dim3((unsigned)grid),
                        dim3(64 * WM * WN), 0, st, a);
   return hipGetLastError();
-}
-
-// Segments with the same weight format share one launch; a mixed pair (MXFP4
-// routed experts + bf16 shared expert) takes one launch per format.
-template <int BM, int BN, int WM, int WN, int P>
-static hipError_t launch_bf16_cfg(const GemmArgs& a, bool gated, hipStream_t st) {
-  if (a.nseg == 1 || a.seg[0].wfmt == a.seg[1].wfmt) {
-    return a.seg[0].wfmt ? launch_one<BM, BN, WM, WN, P, true>(a, gated, st)
-                         : launch_one<BM, BN, WM, WN, P, false>(a, gated, st);
-  }
-  for (int i = 0; i < 2; ++i) {
-    GemmArgs one{};
-    one.seg[0] = a.seg[i];
-    one.nseg = 1;
-    hipError_t e = one.seg[0].wfmt ? launch_one<BM, BN, WM, WN, P, true>(one, gated, st)
-                                   : launch_one<BM, BN, WM, WN, P, false>(one, gated, st);
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
 }
 
 // Tile configurations (BM token rows, BN features, WM x WN waves, P stages in
@@ -513,53 +445,210 @@ enum TileCfg {
   TILE_64x32_2x2,
   TILE_64x64_4x1_P2,
   TILE_32x64_2x2,
-  TILE_COUNT
+  TILE_64x128_2x2,
+  TILE_64x128_1x4,
+  TILE_64x16_4x1,
+  TILE_128x16_4x1,
+  TILE_64x32_4x1_P2,
+  TILE_32x64_2x2_P2,
+  TILE_64x64_2x2_P2,
+  TILE_64x128_2x2_P2,
+  TILE_64x64_4x1_P3,
+  TILE_128x64_4x1_P2,
+  TILE_COUNT,
+  TILE_F32 = 100        // fp32 VALU kernel, 16 x 16 tiles
 };
 
-static hipError_t launch_tile_cfg(int cfg, const GemmArgs& a, bool gated, hipStream_t st) {
+struct TileShape {
+  int BM, BN;
+};
+
+static TileShape tile_shape(int cfg) {
   switch (cfg) {
-    case TILE_16x16_1x1: return launch_bf16_cfg<16, 16, 1, 1, 4>(a, gated, st);
-    case TILE_16x32_1x2: return launch_bf16_cfg<16, 32, 1, 2, 4>(a, gated, st);
-    case TILE_16x64_1x4: return launch_bf16_cfg<16, 64, 1, 4, 4>(a, gated, st);
-    case TILE_32x64_1x4: return launch_bf16_cfg<32, 64, 1, 4, 4>(a, gated, st);
-    case TILE_64x64_1x4: return launch_bf16_cfg<64, 64, 1, 4, 4>(a, gated, st);
-    case TILE_64x64_4x1: return launch_bf16_cfg<64, 64, 4, 1, 4>(a, gated, st);
-    case TILE_64x64_2x2: return launch_bf16_cfg<64, 64, 2, 2, 4>(a, gated, st);
-    case TILE_128x64_4x1: return launch_bf16_cfg<128, 64, 4, 1, 3>(a, gated, st);
-    case TILE_128x64_2x2: return launch_bf16_cfg<128, 64, 2, 2, 3>(a, gated, st);
-    case TILE_64x32_4x1: return launch_bf16_cfg<64, 32, 4, 1, 4>(a, gated, st);
-    case TILE_128x32_4x1: return launch_bf16_cfg<128, 32, 4, 1, 4>(a, gated, st);
-    case TILE_32x32_2x1: return launch_bf16_cfg<32, 32, 2, 1, 4>(a, gated, st);
-    case TILE_64x32_2x2: return launch_bf16_cfg<64, 32, 2, 2, 4>(a, gated, st);
-    case TILE_64x64_4x1_P2: return launch_bf16_cfg<64, 64, 4, 1, 2>(a, gated, st);
-    default: return launch_bf16_cfg<32, 64, 2, 2, 4>(a, gated, st);
+    case TILE_16x16_1x1: return {16, 16};
+    case TILE_16x32_1x2: return {16, 32};
+    case TILE_16x64_1x4: return {16, 64};
+    case TILE_32x64_1x4: return {32, 64};
+    case TILE_64x64_1x4: return {64, 64};
+    case TILE_64x64_4x1: return {64, 64};
+    case TILE_64x64_2x2: return {64, 64};
+    case TILE_128x64_4x1: return {128, 64};
+    case TILE_128x64_2x2: return {128, 64};
+    case TILE_64x32_4x1: return {64, 32};
+    case TILE_128x32_4x1: return {128, 32};
+    case TILE_32x32_2x1: return {32, 32};
+    case TILE_64x32_2x2: return {64, 32};
+    case TILE_64x64_4x1_P2: return {64, 64};
+    case TILE_32x64_2x2: return {32, 64};
+    case TILE_64x128_2x2: return {64, 128};
+    case TILE_64x128_1x4: return {64, 128};
+    case TILE_64x16_4x1: return {64, 16};
+    case TILE_128x16_4x1: return {128, 16};
+    case TILE_64x32_4x1_P2: return {64, 32};
+    case TILE_32x64_2x2_P2: return {32, 64};
+    case TILE_64x64_2x2_P2: return {64, 64};
+    case TILE_64x128_2x2_P2: return {64, 128};
+    case TILE_64x64_4x1_P3: return {64, 64};
+    case TILE_128x64_4x1_P2: return {128, 64};
+    default: return {16, 16};  // TILE_F32
+  }
+}
+
+template <bool FP4>
+static hipError_t launch_tile_cfg(int cfg, const GemmArgs& a, bool gated, int64_t grid,
+                                  hipStream_t st) {
+  switch (cfg) {
+    case TILE_16x16_1x1: return launch_one<16, 16, 1, 1, 4, FP4>(a, gated, grid, st);
+    case TILE_16x32_1x2: return launch_one<16, 32, 1, 2, 4, FP4>(a, gated, grid, st);
+    case TILE_16x64_1x4: return launch_one<16, 64, 1, 4, 4, FP4>(a, gated, grid, st);
+    case TILE_32x64_1x4: return launch_one<32, 64, 1, 4, 4, FP4>(a, gated, grid, st);
+    case TILE_64x64_1x4: return launch_one<64, 64, 1, 4, 4, FP4>(a, gated, grid, st);
+    case TILE_64x64_4x1: return launch_one<64, 64, 4, 1, 4, FP4>(a, gated, grid, st);
+    case TILE_64x64_2x2: return launch_one<64, 64, 2, 2, 4, FP4>(a, gated, grid, st);
+    case TILE_128x64_4x1: return launch_one<128, 64, 4, 1, 3, FP4>(a, gated, grid, st);
+    case TILE_128x64_2x2: return launch_one<128, 64, 2, 2, 3, FP4>(a, gated, grid, st);
+    case TILE_64x32_4x1: return launch_one<64, 32, 4, 1, 4, FP4>(a, gated, grid, st);
+    case TILE_128x32_4x1: return launch_one<128, 32, 4, 1, 4, FP4>(a, gated, grid, st);
+    case TILE_32x32_2x1: return launch_one<32, 32, 2, 1, 4, FP4>(a, gated, grid, st);
+    case TILE_64x32_2x2: return launch_one<64, 32, 2, 2, 4, FP4>(a, gated, grid, st);
+    case TILE_64x64_4x1_P2: return launch_one<64, 64, 4, 1, 2, FP4>(a, gated, grid, st);
+    case TILE_32x64_2x2: return launch_one<32, 64, 2, 2, 4, FP4>(a, gated, grid, st);
+    case TILE_64x128_2x2: return launch_one<64, 128, 2, 2, 4, FP4>(a, gated, grid, st);
+    case TILE_64x128_1x4: return launch_one<64, 128, 1, 4, 4, FP4>(a, gated, grid, st);
+    case TILE_64x16_4x1: return launch_one<64, 16, 4, 1, 4, FP4>(a, gated, grid, st);
+    case TILE_128x16_4x1: return launch_one<128, 16, 4, 1, 4, FP4>(a, gated, grid, st);
+    case TILE_64x32_4x1_P2: return launch_one<64, 32, 4, 1, 2, FP4>(a, gated, grid, st);
+    case TILE_32x64_2x2_P2: return launch_one<32, 64, 2, 2, 2, FP4>(a, gated, grid, st);
+    case TILE_64x64_2x2_P2: return launch_one<64, 64, 2, 2, 2, FP4>(a, gated, grid, st);
+    case TILE_64x128_2x2_P2: return launch_one<64, 128, 2, 2, 2, FP4>(a, gated, grid, st);
+    case TILE_64x64_4x1_P3: return launch_one<64, 64, 4, 1, 3, FP4>(a, gated, grid, st);
+    case TILE_128x64_4x1_P2: return launch_one<128, 64, 4, 1, 2, FP4>(a, gated, grid, st);
+    default: return hipErrorInvalidValue;
   }
 }
 
 // Host-side choice from the average rows per group (no device sync), from
 // measured sweeps on MI355X (all choices give identical bits).
-static int pick_tile_cfg(const GemmArgs& a, bool gated, int64_t rows_per_group_hint) {
-  (void)a;
+static int pick_tile_cfg(bool gated, int64_t rows_per_group_hint) {
   if (rows_per_group_hint <= 2) return gated ? TILE_16x32_1x2 : TILE_16x64_1x4;
   if (rows_per_group_hint <= 16) return TILE_32x64_1x4;
-  if (rows_per_group_hint <= 96) return gated ? TILE_64x32_4x1 : TILE_64x64_4x1;
+  if (rows_per_group_hint <= 96) return gated ? TILE_64x32_4x1_P2 : TILE_64x64_4x1_P2;
   return gated ? TILE_128x64_2x2 : TILE_128x64_4x1;
 }
 
-hipError_t launch_grouped_gemm(const GemmArgs& a, bool gated, int act, int64_t rows_per_group_hint,
-                               hipStream_t st) {
-  if (act == MOE_F32) {
+GemmPlan plan_grouped_gemm(const SegShape* segs, int nseg, bool gated, int act,
+                           int64_t rows_per_group_hint) {
+  GemmPlan p{};
+  p.valid = true;
+  p.gated = gated;
+  p.act = act;
+  p.nseg = nseg;
+  for (int i = 0; i < nseg; ++i) p.seg[i] = segs[i];
+  const int cfg = act == MOE_F32 ? (int)TILE_F32 : pick_tile_cfg(gated, rows_per_group_hint);
+  const TileShape ts = tile_shape(cfg);
+  // Segments with the same weight format share one launch; a mixed pair
+  // (MXFP4 routed experts + bf16 shared expert) takes one launch per format.
+  const bool split = nseg == 2 && segs[0].wfmt != segs[1].wfmt;
+  const int nl = split ? 2 : 1;
+  for (int l = 0; l < nl; ++l) {
+    PlanLaunch& L = p.l[p.n];
+    L.seg_mask = split ? (1 << l) : (nseg == 2 ? 3 : 1);
+    L.cfg = cfg;
+    L.BM = ts.BM;
+    L.BN = ts.BN;
     int64_t tiles = 0;
-    for (int i = 0; i < a.nseg; ++i) tiles += seg_tile_bound(a.seg[i], 16, 16);
-    if (tiles == 0) return hipSuccess;
-    const int64_t grid = (tiles + 7) / 8 * 8;
-    if (gated)
-      hipLaunchKernelGGL(k_grouped_gemm_f32<true>, dim3((unsigned)grid), dim3(256), 0, st, a);
-    else
-      hipLaunchKernelGGL(k_grouped_gemm_f32<false>, dim3((unsigned)grid), dim3(256), 0, st, a);
-    return hipGetLastError();
+    for (int i = 0; i < nseg; ++i)
+      if (L.seg_mask & (1 << i)) tiles += seg_tile_bound(segs[i], ts.BM, ts.BN);
+    L.grid = (tiles + 7) / 8 * 8;
+    if (L.grid > 0x7ffffff8) p.valid = false;  // one launch holds < 2^31 workgroups
+    if (L.grid > 0) ++p.n;
   }
-  return launch_tile_cfg(pick_tile_cfg(a, gated, rows_per_group_hint), a, gated, st);
+  return p;
+}
+
+int64_t plan_table_entries(const GemmPlan& p) {
+  int64_t n = 0;
+  for (int i = 0; i < p.n; ++i) n += p.l[i].grid;
+  return n;
+}
+
+bool plan_tile_jobs(const GemmPlan& p, int4* tables, TileJobs& jobs) {
+  for (int i = 0; i < p.n; ++i) {
+    const PlanLaunch& L = p.l[i];
+    if (jobs.n == MOE_MAX_TILE_JOBS || (jobs.n > 0 && jobs.BM != L.BM)) return false;
+    jobs.BM = L.BM;
+    TileJob& J = jobs.job[jobs.n++];
+    J = TileJob{};
+    J.table = tables;
+    J.grid = L.grid;
+    J.BM = L.BM;
+    J.BN = L.BN;
+    for (int sg = 0; sg < p.nseg; ++sg) {
+      if (!(L.seg_mask & (1 << sg))) continue;
+      J.grouped[J.nseg] = p.seg[sg].grouped ? 1 : 0;
+      J.M[J.nseg] = p.seg[sg].M;
+      J.N[J.nseg] = p.seg[sg].N;
+      ++J.nseg;
+    }
+    tables += L.grid;
+  }
+  return true;
+}
+
+hipError_t launch_grouped_gemm(const GemmPlan& p, const GemmArgs& a, int4* tables,
+                               hipStream_t st) {
+  for (int i = 0; i < p.n; ++i) {
+    const PlanLaunch& L = p.l[i];
+    GemmArgs one{};
+    for (int sg = 0; sg < a.nseg; ++sg)
+      if (L.seg_mask & (1 << sg)) one.seg[one.nseg++] = a.seg[sg];
+    one.tiles = tables;
+    hipError_t e;
+    if (L.cfg == TILE_F32) {
+      if (p.gated)
+        hipLaunchKernelGGL(k_grouped_gemm_f32<true>, dim3((unsigned)L.grid), dim3(256), 0, st, one);
+      else
+        hipLaunchKernelGGL(k_grouped_gemm_f32<false>, dim3((unsigned)L.grid), dim3(256), 0, st, one);
+      e = hipGetLastError();
+    } else {
+      e = one.seg[0].wfmt ? launch_tile_cfg<true>(L.cfg, one, p.gated, L.grid, st)
+                          : launch_tile_cfg<false>(L.cfg, one, p.gated, L.grid, st);
+    }
+    if (e != hipSuccess) return e;
+    tables += L.grid;
+  }
+  return hipSuccess;
+}
+
+// Standalone table builder (caller-supplied offsets): one workgroup.
+__global__ __launch_bounds__(1024) void k_tile_tables(const int32_t* __restrict__ offsets, int E,
+                                                      TileJobs jobs) {
+  __shared__ int soff[MOE_MAX_EXPERTS + 1];
+  __shared__ int mpre[MOE_MAX_EXPERTS + 1];
+  __shared__ int unused[MOE_MAX_EXPERTS + 1];
+  __shared__ int wsum[2 * (1024 / 64)];
+  __shared__ int omap[kTileOwnerMax];
+  for (int e = threadIdx.x; e <= E; e += 1024) soff[e] = offsets[e];
+  __syncthreads();
+  // m-tile counts of the grouped segment (the same rows in every job)
+  int64_t M = 0;
+  for (int j = 0; j < jobs.n; ++j)
+    for (int sg = 0; sg < jobs.job[j].nseg; ++sg)
+      if (jobs.job[j].grouped[sg]) M = jobs.job[j].M[sg];
+  for (int e = threadIdx.x; e < E; e += 1024) {
+    mpre[e] = (tile_group_rows(soff, e, M) + jobs.BM - 1) / jobs.BM;
+    unused[e] = 0;
+  }
+  __syncthreads();
+  tile_scan2<1024>(mpre, unused, E, wsum);
+  const bool map = build_tile_owner<1024>(mpre, E, omap);
+  build_tile_tables<1024>(jobs, soff, mpre, map ? omap : nullptr, E);
+}
+
+hipError_t launch_tile_tables(const int32_t* offsets, int E, const TileJobs& jobs, hipStream_t s) {
+  if (jobs.n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_tile_tables, dim3(1), dim3(1024), 0, s, offsets, E, jobs);
+  return hipGetLastError();
 }
 
 }  // namespace moe

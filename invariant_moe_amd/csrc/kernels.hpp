@@ -25,9 +25,57 @@ struct GemmSeg {
   void* out;               // [rows, N]
 };
 
+// Tile descriptor, one per workgroup of a GEMM launch (int4):
+//   x = first output row, y = valid rows (0: the workgroup has no tile),
+//   z = (segment << 16) | group, w = first output feature.
 struct GemmArgs {
   GemmSeg seg[2];
   int nseg;
+  const int4* tiles;  // [grid] descriptors, indexed by blockIdx.x
+};
+
+// Shape of a segment as the host planner sees it.
+struct SegShape {
+  bool grouped;  // rows grouped by device offsets (E groups); else one group of M rows
+  int64_t M;
+  int G, K, N;
+  int wfmt;
+};
+
+// One launch of a planned grouped GEMM.
+struct PlanLaunch {
+  int seg_mask;  // which segments of the GEMM this launch covers
+  int cfg;       // kernel configuration (tile shape)
+  int BM, BN;
+  int64_t grid;  // workgroups = tile-table entries
+};
+
+struct GemmPlan {
+  PlanLaunch l[2];
+  int n;
+  bool valid;  // false: a launch would exceed the grid limit
+  bool gated;
+  int act;
+  SegShape seg[2];
+  int nseg;
+};
+
+// Tile-table job: the device writes the descriptors of one launch.
+struct TileJob {
+  int4* table;
+  int64_t grid;
+  int BM, BN;
+  int nseg;
+  int grouped[2];  // 1: E groups from the device offsets; 0: one group of M rows
+  int64_t M[2];
+  int N[2];
+};
+
+constexpr int MOE_MAX_TILE_JOBS = 4;
+struct TileJobs {
+  TileJob job[MOE_MAX_TILE_JOBS];
+  int n;
+  int BM;  // row tile shared by every job
 };
 
 // zero_mask (optional): E * ceil(T/64) words cleared for launch_topk's mask.
@@ -40,13 +88,25 @@ hipError_t launch_hash_route(const int32_t* token_ids, int64_t T, int E, int k, 
 hipError_t launch_routing_scores(const float* in, int64_t n, int mode, float* out, hipStream_t s);
 hipError_t launch_mask_from_idx(const int32_t* topk_idx, int64_t T, int k, int E, uint64_t* mask,
                                 hipStream_t s);
+// jobs (optional): tile tables written from the new offsets in the same launch.
 hipError_t launch_permute(const int32_t* topk_idx, int64_t T, int k, int E, const uint64_t* mask,
                           int32_t* wprefix, int32_t* counts, int32_t* offsets, int32_t* row_token,
-                          int32_t* pair_row, hipStream_t s);
+                          int32_t* pair_row, const TileJobs* jobs, hipStream_t s);
 hipError_t launch_gather_rows(const void* x, const int32_t* row_token, int64_t T, int64_t R,
                               int64_t row_bytes, void* out, hipStream_t s);
-hipError_t launch_grouped_gemm(const GemmArgs& a, bool gated, int act,
-                               int64_t rows_per_group_hint, hipStream_t s);
+// Tile tables from caller-supplied offsets [E+1] (one small launch).
+hipError_t launch_tile_tables(const int32_t* offsets, int E, const TileJobs& jobs, hipStream_t s);
+
+// Host planning of a grouped GEMM (tile shape, launches, table sizes).
+GemmPlan plan_grouped_gemm(const SegShape* segs, int nseg, bool gated, int act,
+                           int64_t rows_per_group_hint);
+int64_t plan_table_entries(const GemmPlan& p);
+// Appends the table jobs of p (tables carved from `tables`, plan_table_entries(p) entries).
+// Returns false when p's row tile differs from the jobs already appended.
+bool plan_tile_jobs(const GemmPlan& p, int4* tables, TileJobs& jobs);
+// Launches the planned GEMM; a.tiles is ignored (each launch uses its own table).
+hipError_t launch_grouped_gemm(const GemmPlan& p, const GemmArgs& a, int4* tables, hipStream_t s);
+
 hipError_t launch_combine(const void* expert_out, const int32_t* topk_idx, const float* topk_w,
                           const int32_t* pair_row, const void* shared_out, int64_t T, int k,
                           int D, int act, void* y, hipStream_t s);

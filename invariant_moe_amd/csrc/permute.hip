@@ -12,6 +12,7 @@
 // so rows of an expert are in ascending token order, as the counting sort.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "tiles.hpp"
 
 namespace moe {
 
@@ -35,35 +36,8 @@ __global__ __launch_bounds__(256) void k_mask_from_idx(const int32_t* __restrict
   for (int e = threadIdx.x; e < E; e += 256) mask[(int64_t)e * W + tb] = smask[e];
 }
 
-// Exclusive scan of n <= 1024 ints in LDS by a 1024-thread block.
-__device__ void block_exclusive_scan_1024(int* s, int n, int* total) {
-  __shared__ int wsum[16];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int v = tid < n ? s[tid] : 0;
-  int incl = v;
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    int o = __shfl_up(incl, m);
-    if (lane >= m) incl += o;
-  }
-  if (lane == 63) wsum[wave] = incl;
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int i = 0; i < 16; ++i) {
-      int x = wsum[i];
-      wsum[i] = run;
-      run += x;
-    }
-    *total = run;
-  }
-  __syncthreads();
-  if (tid < n) s[tid] = wsum[wave] + incl - v;
-  __syncthreads();
-}
-
-// counts, offsets, per-(expert, block) prefixes, then the scatter.  One
-// workgroup of 1024 threads.
+// counts, offsets, per-(expert, block) prefixes, the tile tables of the
+// grouped GEMMs that follow, then the scatter.  One workgroup of 1024 threads.
 __global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ topk_idx,
                                                   int64_t T, int k, int E,
                                                   const uint64_t* __restrict__ mask, int64_t W,
@@ -71,40 +45,74 @@ __global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ to
                                                   int32_t* __restrict__ counts,
                                                   int32_t* __restrict__ offsets,
                                                   int32_t* __restrict__ row_token,
-                                                  int32_t* __restrict__ pair_row) {
-  __shared__ int soff[MOE_MAX_EXPERTS];
-  __shared__ int stotal;
+                                                  int32_t* __restrict__ pair_row,
+                                                  TileJobs jobs) {
+  __shared__ int soff[MOE_MAX_EXPERTS + 1];
+  __shared__ int mpre[MOE_MAX_EXPERTS + 1];
+  __shared__ int wsum[2 * (1024 / 64)];
+  __shared__ int omap[kTileOwnerMax];
+  const int BM = jobs.n > 0 ? jobs.BM : 1;
   const int tid = threadIdx.x;
   for (int e = tid; e < E; e += 1024) {
     int c = 0;
     const uint64_t* me = mask + (int64_t)e * W;
     int32_t* pe = wprefix + (int64_t)e * W;
-    for (int64_t b = 0; b < W; ++b) {
-      pe[b] = c;
-      c += __popcll(me[b]);
+    for (int b0 = 0; b0 < (int)W; b0 += 8) {  // eight mask words in flight
+      uint64_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = b0 + u < W ? me[b0 + u] : 0ull;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (b0 + u < W) pe[b0 + u] = c;
+        c += __popcll(v[u]);
+      }
     }
     counts[e] = c;
     soff[e] = c;
+    mpre[e] = (c + BM - 1) / BM;
   }
   __syncthreads();
-  block_exclusive_scan_1024(soff, E, &stotal);
-  for (int e = tid; e < E; e += 1024) offsets[e] = soff[e];
-  if (tid == 0) offsets[E] = stotal;
+  tile_scan2<1024>(soff, mpre, E, wsum);
+  for (int e = tid; e <= E; e += 1024) offsets[e] = soff[e];
+  if (jobs.n > 0) {
+    const bool map = build_tile_owner<1024>(mpre, E, omap);
+    build_tile_tables<1024>(jobs, soff, mpre, map ? omap : nullptr, E);
+  }
   // wprefix written above by this workgroup is visible after the barrier.
-  const int64_t R = T * k;
-  for (int64_t p = tid; p < R; p += 1024) {
-    const int64_t t = p / k;
-    const int e = topk_idx[p];
-    if (e < 0 || e >= E) {  // outside the contract; keep memory safe
-      pair_row[p] = -1;
-      continue;
+  // Four pairs per thread per round, their loads issued together; indices
+  // fit in 32 bits (T * k < 2^31).
+  const unsigned R = (unsigned)(T * k), uk = (unsigned)k;
+  for (unsigned p0 = tid; p0 < R; p0 += 4 * 1024) {
+    int e[4];
+    uint64_t word[4];
+    int32_t pre_b[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const unsigned p = p0 + u * 1024;
+      e[u] = p < R ? topk_idx[p] : -1;
     }
-    const int64_t b = t >> 6;
-    const uint64_t word = mask[(int64_t)e * W + b];
-    const uint64_t below = word & ((1ull << (t & 63)) - 1ull);
-    const int32_t r = soff[e] + wprefix[(int64_t)e * W + b] + __popcll(below);
-    row_token[r] = (int32_t)t;
-    pair_row[p] = r;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const unsigned p = p0 + u * 1024;
+      const bool valid = p < R && e[u] >= 0 && e[u] < E;
+      const int64_t at = valid ? (int64_t)e[u] * W + ((p / uk) >> 6) : 0;
+      word[u] = valid ? mask[at] : 0ull;
+      pre_b[u] = valid ? wprefix[at] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const unsigned p = p0 + u * 1024;
+      if (p >= R) continue;
+      if (e[u] < 0 || e[u] >= E) {  // outside the contract; keep memory safe
+        pair_row[p] = -1;
+        continue;
+      }
+      const unsigned t = p / uk;
+      const uint64_t below = word[u] & ((1ull << (t & 63)) - 1ull);
+      const int32_t r = soff[e[u]] + pre_b[u] + __popcll(below);
+      row_token[r] = (int32_t)t;
+      pair_row[p] = r;
+    }
   }
 }
 
@@ -136,10 +144,11 @@ hipError_t launch_mask_from_idx(const int32_t* topk_idx, int64_t T, int k, int E
 
 hipError_t launch_permute(const int32_t* topk_idx, int64_t T, int k, int E, const uint64_t* mask,
                           int32_t* wprefix, int32_t* counts, int32_t* offsets, int32_t* row_token,
-                          int32_t* pair_row, hipStream_t s) {
+                          int32_t* pair_row, const TileJobs* jobs, hipStream_t s) {
   const int64_t W = (T + 63) / 64;
+  TileJobs none{};
   hipLaunchKernelGGL(k_permute, dim3(1), dim3(1024), 0, s, topk_idx, T, k, E, mask, W, wprefix,
-                     counts, offsets, row_token, pair_row);
+                     counts, offsets, row_token, pair_row, jobs ? *jobs : none);
   return hipGetLastError();
 }
 
