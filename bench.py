@@ -41,6 +41,11 @@ def parse():
     p.add_argument("--config", type=int, default=2, help="layer recipe (1..5), default 2")
     p.add_argument("--T", type=int, default=None, help="override the batch size")
     p.add_argument("--replicas", type=int, default=0, help="weight replicas (0 = auto)")
+    p.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV",
+                                                          "CAL_FETCH_CSV", "CAL_WRITE_CSV"),
+                   help="turn rocprofv3 --pmc counter CSVs (FETCH_SIZE run, WRITE_SIZE run, and "
+                        "the same two counters over --copy-calibration) into the gate/up GEMM "
+                        "HBM bytes per launch; writes profiles/gate_up_gemm_traffic.json")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="approximate CPU time budget of the oracle baseline (0 = skip)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -94,6 +99,47 @@ def measured_traffic(per_launch_bytes_alg: float):
     return d.get("bytes_per_launch")
 
 
+def _counter_means(path, counter, name_pred):
+    import csv
+    vals = []
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] == counter and name_pred(row["Kernel_Name"]):
+                vals.append(float(row["Counter_Value"]))
+    return vals
+
+
+def traffic_summary(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the gate/up GEMM, each
+    scaled by the bytes a 1 GiB device copy really moves over what the same
+    counter reports for it."""
+    gated = lambda n: "k_grouped_gemm_bf16<" in n and ", true, " in n
+    copy = lambda n: "copyBuffer" in n
+    f = _counter_means(fetch_csv, "FETCH_SIZE", gated)
+    w = _counter_means(write_csv, "WRITE_SIZE", gated)
+    cf = _counter_means(cal_fetch_csv, "FETCH_SIZE", copy)
+    cw = _counter_means(cal_write_csv, "WRITE_SIZE", copy)
+    if not (f and w and cf and cw):
+        raise SystemExit("traffic summary: missing counter rows")
+    n = float(1 << 30)
+    kf = n / (sum(cf) / len(cf) * 1024.0)
+    kw = n / (sum(cw) / len(cw) * 1024.0)
+    fetch = sum(f) / len(f) * 1024.0 * kf
+    write = sum(w) / len(w) * 1024.0 * kw
+    d = {"kernel": "k_grouped_gemm_bf16 gate/up (gated) launch",
+         "kernel_source_hash": kernel_source_hash(),
+         "dispatches": [len(f), len(w)],
+         "fetch_size_kib_avg": round(sum(f) / len(f), 1),
+         "write_size_kib_avg": round(sum(w) / len(w), 1),
+         "copy_factor_fetch": round(kf, 4), "copy_factor_write": round(kw, 4),
+         "fetch_bytes_per_launch": int(fetch), "write_bytes_per_launch": int(write),
+         "bytes_per_launch": int(fetch + write)}
+    with open(PROFILE_TRAFFIC, "w") as fh:
+        json.dump(d, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(d))
+
+
 def copy_calibration():
     import torch
     n = 1 << 30
@@ -109,11 +155,14 @@ def copy_calibration():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); "
-              "the multi-GPU sharding is described in DESIGN.md, not run.", file=sys.stderr)
+        print(f"bench.py: measures one GPU only (--gpus {args.gpus} requested); the layer is "
+              "not sharded across GPUs here.", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary)
         return
 
     import numpy as np
@@ -164,25 +213,46 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    evs = [[hip.event() for _ in range(6)] for _ in range(K)]
+    # Pass 1 (the measurement): K steps with no instrumentation inside; one
+    # event pair and the host clock bracket them.
     ev0, ev1 = hip.event(), hip.event()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     hip.record(ev0, sptr)
     for i in range(K):
-        moe.set_stage_events(evs[i])
         layers[i % nrep].forward(x, ids, out=y)
-    moe.set_stage_events(None)
     hip.record(ev1, sptr)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = hip.elapsed_ms(ev0, ev1)
     ms_per_step = max(wall * 1e3, gpu_ms) / K
 
+    # Pass 2: the same steps with events between the stages (each event
+    # record costs GPU time, so these sum to more than a step of pass 1).
+    evs = [[hip.event() for _ in range(6)] for _ in range(K)]
+    for i in range(K):
+        moe.set_stage_events(evs[i])
+        layers[i % nrep].forward(x, ids, out=y)
+    moe.set_stage_events(None)
+    torch.cuda.synchronize()
     stage_ms = np.array([[hip.elapsed_ms(evs[i][s], evs[i][s + 1]) for s in range(5)]
                          for i in range(K)])
     stage_avg = stage_ms.mean(0)
-    gu_ms = float(stage_avg[2])
+    # Pass 3: kernel-only time of the two GEMM launches, from events recorded
+    # at the kernels' own start and end (hipExtLaunchKernel).
+    K2 = min(K, 50)
+    kev = [[hip.event() for _ in range(10)] for _ in range(K2)]
+    for i in range(K2):
+        moe.set_stage_events(kev[i])
+        layers[i % nrep].forward(x, ids, out=y)
+    moe.set_stage_events(None)
+    torch.cuda.synchronize()
+    try:
+        kern_ms = np.array([[hip.elapsed_ms(kev[i][6], kev[i][7]),
+                             hip.elapsed_ms(kev[i][8], kev[i][9])] for i in range(K2)]).mean(0)
+    except AssertionError:  # a library without kernel events: stage times instead
+        kern_ms = stage_avg[[2, 3]]
+    gu_ms = float(kern_ms[0])
 
     # algorithmic work of the gate/up SwiGLU GEMM launch (routed + shared groups)
     T, D, E, k, I, Is = cfg.T, cfg.D, cfg.E, cfg.k, cfg.I, cfg.I_shared
@@ -275,6 +345,8 @@ def main():
                   "hbm_frac": round(layer_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                   "tflops": round(layer_flops / (ms_per_step * 1e-3) / 1e12, 2),
                   "stage_ms": {n: round(float(v), 5) for n, v in zip(moe.STAGES, stage_avg)},
+                  "kernel_ms": {"gate_up_gemm": round(float(kern_ms[0]), 5),
+                                "down_gemm": round(float(kern_ms[1]), 5)},
                   "gpu_event_ms_per_step": round(gpu_ms / K, 5)},
     }
     print(json.dumps(out), flush=True)

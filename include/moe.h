@@ -220,10 +220,15 @@ int moe_layer_forward(const void* x, const int32_t* token_ids, const void* w_rou
  * calls on this host thread record events[0] before the first kernel and
  * events[i+1] after stage i on the call's stream; stages: 0 routing,
  * 1 permutation, 2 gate/up SwiGLU GEMM, 3 down GEMM, 4 combine
- * (MOE_STAGE_EVENTS events).  The events are hipEvent_t handles created by the
- * caller; pass NULL / 0 to stop recording.
+ * (MOE_STAGE_EVENTS events).  With MOE_STAGE_EVENTS + MOE_KERNEL_EVENTS events,
+ * events[6] / events[7] also mark the start / end of the gate/up GEMM kernel
+ * itself and events[8] / events[9] those of the down GEMM kernel (kernel time
+ * without the launch gaps the stage events include; hipExtLaunchKernel).
+ * The events are hipEvent_t handles created by the caller; pass NULL / 0 to
+ * stop recording.
  * ------------------------------------------------------------------------- */
 #define MOE_STAGE_EVENTS 6
+#define MOE_KERNEL_EVENTS 4
 int moe_set_stage_events(void* const* events, int n_events);
 
 const char* moe_status_string(int status);

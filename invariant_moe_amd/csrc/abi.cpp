@@ -150,6 +150,11 @@ int check_act(moe_dtype act) {
   return MOE_OK;
 }
 
+hipEvent_t kernel_event(int i) {
+  return (g_stage_events && i < g_n_stage_events) ? static_cast<hipEvent_t>(g_stage_events[i])
+                                                  : nullptr;
+}
+
 void record_stage(int i, hipStream_t s) {
   if (g_stage_events && i < g_n_stage_events && g_stage_events[i])
     (void)hipEventRecord(static_cast<hipEvent_t>(g_stage_events[i]), s);
@@ -235,8 +240,9 @@ int moe_router_topk(const void* x, moe_dtype act, const void* w_router, const fl
   if (workspace && !aligned(workspace, 16)) return fail(MOE_ERR_ALIGN, "workspace misaligned");
   if (T == 0) return ok();
   float* logits = static_cast<float*>(workspace);
-  hipError_t e = moe::launch_router_logits(x, act, w_router, T, D, E, logits, nullptr, s);
-  if (e == hipSuccess) e = moe::launch_topk(logits, bias, T, E, k, mode, topk_idx, topk_w, nullptr, s);
+  hipError_t e = moe::launch_router_logits(x, act, w_router, T, D, E, logits, nullptr, 0, s);
+  if (e == hipSuccess)
+    e = moe::launch_topk(logits, bias, T, E, k, mode, topk_idx, topk_w, nullptr, s);
   return hip_status(e, "router");
 }
 
@@ -424,16 +430,6 @@ int moe_layer_forward(const void* x, const int32_t* token_ids, const void* w_rou
   void* sh = ws + L.s;
   const int64_t R = T * k;
 
-  record_stage(0, s);
-  hipError_t e;
-  if (mode == MOE_ROUTE_HASH) {
-    e = moe::launch_hash_route(token_ids, T, E, k, idx, tw, mask, s);
-  } else {
-    e = moe::launch_router_logits(x, act, w_router, T, D, E, logits, mask, s);
-    if (e == hipSuccess) e = moe::launch_topk(logits, bias, T, E, k, mode, idx, tw, mask, s);
-  }
-  if (e != hipSuccess) return hip_status(e, "routing");
-  record_stage(1, s);
   const FfnPlans p = ffn_plans(R, T, D, E, I, Is, act, routed->dtype == MOE_MXFP4 ? 1 : 0,
                                shared && shared->dtype == MOE_MXFP4 ? 1 : 0);
   if (!p.up.valid || !p.dn.valid) return fail(MOE_ERR_SHAPE, "problem too large for one launch");
@@ -444,6 +440,17 @@ int moe_layer_forward(const void* x, const int32_t* token_ids, const void* w_rou
   moe::TileJobs jobs{};
   if (!moe::plan_tile_jobs(p.up, tiles_up, jobs) || !moe::plan_tile_jobs(p.dn, tiles_dn, jobs))
     return fail(MOE_ERR_UNSUPPORTED, "gate/up and down GEMM plans use different row tiles");
+
+  record_stage(0, s);
+  hipError_t e;
+  if (mode == MOE_ROUTE_HASH) {
+    e = moe::launch_hash_route(token_ids, T, E, k, idx, tw, mask, s);
+  } else {
+    e = moe::launch_router_logits(x, act, w_router, T, D, E, logits, mask, E * ((T + 63) / 64), s);
+    if (e == hipSuccess) e = moe::launch_topk(logits, bias, T, E, k, mode, idx, tw, mask, s);
+  }
+  if (e != hipSuccess) return hip_status(e, "routing");
+  record_stage(1, s);
   e = moe::launch_permute(idx, T, k, E, mask, wprefix, counts, offsets, row_token, pair_row, &jobs,
                           s);
   if (e != hipSuccess) return hip_status(e, "permute");
@@ -456,7 +463,8 @@ int moe_layer_forward(const void* x, const int32_t* token_ids, const void* w_rou
     up.seg[1] = make_seg(x, nullptr, nullptr, T, 1, D, Is, shared, true, hs);
     up.nseg = 2;
   }
-  e = moe::launch_grouped_gemm(p.up, up, tiles_up, s);
+  e = moe::launch_grouped_gemm(p.up, up, tiles_up, s, kernel_event(MOE_STAGE_EVENTS),
+                               kernel_event(MOE_STAGE_EVENTS + 1));
   if (e != hipSuccess) return hip_status(e, "gate/up GEMM");
   record_stage(3, s);
 
@@ -467,7 +475,8 @@ int moe_layer_forward(const void* x, const int32_t* token_ids, const void* w_rou
     dn.seg[1] = make_seg(hs, nullptr, nullptr, T, 1, Is, D, shared, false, sh);
     dn.nseg = 2;
   }
-  e = moe::launch_grouped_gemm(p.dn, dn, tiles_dn, s);
+  e = moe::launch_grouped_gemm(p.dn, dn, tiles_dn, s, kernel_event(MOE_STAGE_EVENTS + 2),
+                               kernel_event(MOE_STAGE_EVENTS + 3));
   if (e != hipSuccess) return hip_status(e, "down GEMM");
   record_stage(4, s);
 

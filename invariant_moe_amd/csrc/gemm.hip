@@ -20,6 +20,8 @@
 // weights, same DeepSeek-V4 page section 6.2) are decoded exactly to bf16 in
 // LDS and then go through the same bf16 MFMA chain, so the result equals the
 // bf16 kernel on the decoded weights bit for bit.
+#include <hip/hip_ext.h>
+
 #include <type_traits>
 
 #include "common.hpp"
@@ -415,14 +417,19 @@ static int64_t seg_tile_bound(const SegShape& s, int BM, int BN) {
   return ((s.M + BM - 1) / BM + nonempty) * nt;
 }
 
+struct LaunchEvents {
+  hipEvent_t start, stop;
+};
+
 template <int BM, int BN, int WM, int WN, int P, bool FP4>
-static hipError_t launch_one(const GemmArgs& a, bool gated, int64_t grid, hipStream_t st) {
+static hipError_t launch_one(const GemmArgs& a, bool gated, int64_t grid, hipStream_t st,
+                             LaunchEvents ev) {
   if (gated)
-    hipLaunchKernelGGL((k_grouped_gemm_bf16<BM, BN, WM, WN, P, true, FP4>), dim3((unsigned)grid),
-                       dim3(64 * WM * WN), 0, st, a);
+    hipExtLaunchKernelGGL((k_grouped_gemm_bf16<BM, BN, WM, WN, P, true, FP4>),
+                          dim3((unsigned)grid), dim3(64 * WM * WN), 0, st, ev.start, ev.stop, 0, a);
   else
-    hipLaunchKernelGGL((k_grouped_gemm_bf16<BM, BN, WM, WN, P, false, FP4>), dim3((unsigned)grid),
-                       dim3(64 * WM * WN), 0, st, a);
+    hipExtLaunchKernelGGL((k_grouped_gemm_bf16<BM, BN, WM, WN, P, false, FP4>),
+                          dim3((unsigned)grid), dim3(64 * WM * WN), 0, st, ev.start, ev.stop, 0, a);
   return hipGetLastError();
 }
 
@@ -496,33 +503,33 @@ static TileShape tile_shape(int cfg) {
 
 template <bool FP4>
 static hipError_t launch_tile_cfg(int cfg, const GemmArgs& a, bool gated, int64_t grid,
-                                  hipStream_t st) {
+                                  hipStream_t st, LaunchEvents ev) {
   switch (cfg) {
-    case TILE_16x16_1x1: return launch_one<16, 16, 1, 1, 4, FP4>(a, gated, grid, st);
-    case TILE_16x32_1x2: return launch_one<16, 32, 1, 2, 4, FP4>(a, gated, grid, st);
-    case TILE_16x64_1x4: return launch_one<16, 64, 1, 4, 4, FP4>(a, gated, grid, st);
-    case TILE_32x64_1x4: return launch_one<32, 64, 1, 4, 4, FP4>(a, gated, grid, st);
-    case TILE_64x64_1x4: return launch_one<64, 64, 1, 4, 4, FP4>(a, gated, grid, st);
-    case TILE_64x64_4x1: return launch_one<64, 64, 4, 1, 4, FP4>(a, gated, grid, st);
-    case TILE_64x64_2x2: return launch_one<64, 64, 2, 2, 4, FP4>(a, gated, grid, st);
-    case TILE_128x64_4x1: return launch_one<128, 64, 4, 1, 3, FP4>(a, gated, grid, st);
-    case TILE_128x64_2x2: return launch_one<128, 64, 2, 2, 3, FP4>(a, gated, grid, st);
-    case TILE_64x32_4x1: return launch_one<64, 32, 4, 1, 4, FP4>(a, gated, grid, st);
-    case TILE_128x32_4x1: return launch_one<128, 32, 4, 1, 4, FP4>(a, gated, grid, st);
-    case TILE_32x32_2x1: return launch_one<32, 32, 2, 1, 4, FP4>(a, gated, grid, st);
-    case TILE_64x32_2x2: return launch_one<64, 32, 2, 2, 4, FP4>(a, gated, grid, st);
-    case TILE_64x64_4x1_P2: return launch_one<64, 64, 4, 1, 2, FP4>(a, gated, grid, st);
-    case TILE_32x64_2x2: return launch_one<32, 64, 2, 2, 4, FP4>(a, gated, grid, st);
-    case TILE_64x128_2x2: return launch_one<64, 128, 2, 2, 4, FP4>(a, gated, grid, st);
-    case TILE_64x128_1x4: return launch_one<64, 128, 1, 4, 4, FP4>(a, gated, grid, st);
-    case TILE_64x16_4x1: return launch_one<64, 16, 4, 1, 4, FP4>(a, gated, grid, st);
-    case TILE_128x16_4x1: return launch_one<128, 16, 4, 1, 4, FP4>(a, gated, grid, st);
-    case TILE_64x32_4x1_P2: return launch_one<64, 32, 4, 1, 2, FP4>(a, gated, grid, st);
-    case TILE_32x64_2x2_P2: return launch_one<32, 64, 2, 2, 2, FP4>(a, gated, grid, st);
-    case TILE_64x64_2x2_P2: return launch_one<64, 64, 2, 2, 2, FP4>(a, gated, grid, st);
-    case TILE_64x128_2x2_P2: return launch_one<64, 128, 2, 2, 2, FP4>(a, gated, grid, st);
-    case TILE_64x64_4x1_P3: return launch_one<64, 64, 4, 1, 3, FP4>(a, gated, grid, st);
-    case TILE_128x64_4x1_P2: return launch_one<128, 64, 4, 1, 2, FP4>(a, gated, grid, st);
+    case TILE_16x16_1x1: return launch_one<16, 16, 1, 1, 4, FP4>(a, gated, grid, st, ev);
+    case TILE_16x32_1x2: return launch_one<16, 32, 1, 2, 4, FP4>(a, gated, grid, st, ev);
+    case TILE_16x64_1x4: return launch_one<16, 64, 1, 4, 4, FP4>(a, gated, grid, st, ev);
+    case TILE_32x64_1x4: return launch_one<32, 64, 1, 4, 4, FP4>(a, gated, grid, st, ev);
+    case TILE_64x64_1x4: return launch_one<64, 64, 1, 4, 4, FP4>(a, gated, grid, st, ev);
+    case TILE_64x64_4x1: return launch_one<64, 64, 4, 1, 4, FP4>(a, gated, grid, st, ev);
+    case TILE_64x64_2x2: return launch_one<64, 64, 2, 2, 4, FP4>(a, gated, grid, st, ev);
+    case TILE_128x64_4x1: return launch_one<128, 64, 4, 1, 3, FP4>(a, gated, grid, st, ev);
+    case TILE_128x64_2x2: return launch_one<128, 64, 2, 2, 3, FP4>(a, gated, grid, st, ev);
+    case TILE_64x32_4x1: return launch_one<64, 32, 4, 1, 4, FP4>(a, gated, grid, st, ev);
+    case TILE_128x32_4x1: return launch_one<128, 32, 4, 1, 4, FP4>(a, gated, grid, st, ev);
+    case TILE_32x32_2x1: return launch_one<32, 32, 2, 1, 4, FP4>(a, gated, grid, st, ev);
+    case TILE_64x32_2x2: return launch_one<64, 32, 2, 2, 4, FP4>(a, gated, grid, st, ev);
+    case TILE_64x64_4x1_P2: return launch_one<64, 64, 4, 1, 2, FP4>(a, gated, grid, st, ev);
+    case TILE_32x64_2x2: return launch_one<32, 64, 2, 2, 4, FP4>(a, gated, grid, st, ev);
+    case TILE_64x128_2x2: return launch_one<64, 128, 2, 2, 4, FP4>(a, gated, grid, st, ev);
+    case TILE_64x128_1x4: return launch_one<64, 128, 1, 4, 4, FP4>(a, gated, grid, st, ev);
+    case TILE_64x16_4x1: return launch_one<64, 16, 4, 1, 4, FP4>(a, gated, grid, st, ev);
+    case TILE_128x16_4x1: return launch_one<128, 16, 4, 1, 4, FP4>(a, gated, grid, st, ev);
+    case TILE_64x32_4x1_P2: return launch_one<64, 32, 4, 1, 2, FP4>(a, gated, grid, st, ev);
+    case TILE_32x64_2x2_P2: return launch_one<32, 64, 2, 2, 2, FP4>(a, gated, grid, st, ev);
+    case TILE_64x64_2x2_P2: return launch_one<64, 64, 2, 2, 2, FP4>(a, gated, grid, st, ev);
+    case TILE_64x128_2x2_P2: return launch_one<64, 128, 2, 2, 2, FP4>(a, gated, grid, st, ev);
+    case TILE_64x64_4x1_P3: return launch_one<64, 64, 4, 1, 3, FP4>(a, gated, grid, st, ev);
+    case TILE_128x64_4x1_P2: return launch_one<128, 64, 4, 1, 2, FP4>(a, gated, grid, st, ev);
     default: return hipErrorInvalidValue;
   }
 }
@@ -596,23 +603,26 @@ bool plan_tile_jobs(const GemmPlan& p, int4* tables, TileJobs& jobs) {
 }
 
 hipError_t launch_grouped_gemm(const GemmPlan& p, const GemmArgs& a, int4* tables,
-                               hipStream_t st) {
+                               hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop) {
   for (int i = 0; i < p.n; ++i) {
     const PlanLaunch& L = p.l[i];
     GemmArgs one{};
     for (int sg = 0; sg < a.nseg; ++sg)
       if (L.seg_mask & (1 << sg)) one.seg[one.nseg++] = a.seg[sg];
     one.tiles = tables;
+    const LaunchEvents ev{i == 0 ? ev_start : nullptr, i == p.n - 1 ? ev_stop : nullptr};
     hipError_t e;
     if (L.cfg == TILE_F32) {
       if (p.gated)
-        hipLaunchKernelGGL(k_grouped_gemm_f32<true>, dim3((unsigned)L.grid), dim3(256), 0, st, one);
+        hipExtLaunchKernelGGL(k_grouped_gemm_f32<true>, dim3((unsigned)L.grid), dim3(256), 0, st,
+                              ev.start, ev.stop, 0, one);
       else
-        hipLaunchKernelGGL(k_grouped_gemm_f32<false>, dim3((unsigned)L.grid), dim3(256), 0, st, one);
+        hipExtLaunchKernelGGL(k_grouped_gemm_f32<false>, dim3((unsigned)L.grid), dim3(256), 0, st,
+                              ev.start, ev.stop, 0, one);
       e = hipGetLastError();
     } else {
-      e = one.seg[0].wfmt ? launch_tile_cfg<true>(L.cfg, one, p.gated, L.grid, st)
-                          : launch_tile_cfg<false>(L.cfg, one, p.gated, L.grid, st);
+      e = one.seg[0].wfmt ? launch_tile_cfg<true>(L.cfg, one, p.gated, L.grid, st, ev)
+                          : launch_tile_cfg<false>(L.cfg, one, p.gated, L.grid, st, ev);
     }
     if (e != hipSuccess) return e;
     tables += L.grid;

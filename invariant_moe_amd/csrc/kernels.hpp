@@ -78,9 +78,11 @@ struct TileJobs {
   int BM;  // row tile shared by every job
 };
 
-// zero_mask (optional): E * ceil(T/64) words cleared for launch_topk's mask.
+// zero / n_zero (optional): 64-bit words cleared for a later kernel of the call.
 hipError_t launch_router_logits(const void* x, int act, const void* w, int64_t T, int D, int E,
-                                float* logits, uint64_t* zero_mask, hipStream_t s);
+                                float* logits, uint64_t* zero, int64_t n_zero, hipStream_t s);
+// mask (optional): bit t%64 of word [e][t/64] is ORed in for each selected
+// (token t, expert e); the words must be zero at launch.
 hipError_t launch_topk(const float* logits, const float* bias, int64_t T, int E, int k, int mode,
                        int32_t* idx, float* w, uint64_t* mask, hipStream_t s);
 hipError_t launch_hash_route(const int32_t* token_ids, int64_t T, int E, int k, int32_t* idx,
@@ -105,7 +107,10 @@ int64_t plan_table_entries(const GemmPlan& p);
 // Returns false when p's row tile differs from the jobs already appended.
 bool plan_tile_jobs(const GemmPlan& p, int4* tables, TileJobs& jobs);
 // Launches the planned GEMM; a.tiles is ignored (each launch uses its own table).
-hipError_t launch_grouped_gemm(const GemmPlan& p, const GemmArgs& a, int4* tables, hipStream_t s);
+// ev_start / ev_stop (optional) are recorded at the start of the first and the
+// end of the last kernel of the plan.
+hipError_t launch_grouped_gemm(const GemmPlan& p, const GemmArgs& a, int4* tables, hipStream_t s,
+                               hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
 hipError_t launch_combine(const void* expert_out, const int32_t* topk_idx, const float* topk_w,
                           const int32_t* pair_row, const void* shared_out, int64_t T, int k,

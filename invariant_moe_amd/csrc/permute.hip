@@ -12,7 +12,7 @@
 // so rows of an expert are in ascending token order, as the counting sort.
 #include "common.hpp"
 #include "kernels.hpp"
-#include "tiles.hpp"
+#include "permute_core.hpp"
 
 namespace moe {
 
@@ -36,8 +36,6 @@ __global__ __launch_bounds__(256) void k_mask_from_idx(const int32_t* __restrict
   for (int e = threadIdx.x; e < E; e += 256) mask[(int64_t)e * W + tb] = smask[e];
 }
 
-// counts, offsets, per-(expert, block) prefixes, the tile tables of the
-// grouped GEMMs that follow, then the scatter.  One workgroup of 1024 threads.
 __global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ topk_idx,
                                                   int64_t T, int k, int E,
                                                   const uint64_t* __restrict__ mask, int64_t W,
@@ -47,74 +45,11 @@ __global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ to
                                                   int32_t* __restrict__ row_token,
                                                   int32_t* __restrict__ pair_row,
                                                   TileJobs jobs) {
-  __shared__ int soff[MOE_MAX_EXPERTS + 1];
-  __shared__ int mpre[MOE_MAX_EXPERTS + 1];
-  __shared__ int wsum[2 * (1024 / 64)];
-  __shared__ int omap[kTileOwnerMax];
-  const int BM = jobs.n > 0 ? jobs.BM : 1;
-  const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += 1024) {
-    int c = 0;
-    const uint64_t* me = mask + (int64_t)e * W;
-    int32_t* pe = wprefix + (int64_t)e * W;
-    for (int b0 = 0; b0 < (int)W; b0 += 8) {  // eight mask words in flight
-      uint64_t v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = b0 + u < W ? me[b0 + u] : 0ull;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (b0 + u < W) pe[b0 + u] = c;
-        c += __popcll(v[u]);
-      }
-    }
-    counts[e] = c;
-    soff[e] = c;
-    mpre[e] = (c + BM - 1) / BM;
-  }
-  __syncthreads();
-  tile_scan2<1024>(soff, mpre, E, wsum);
-  for (int e = tid; e <= E; e += 1024) offsets[e] = soff[e];
-  if (jobs.n > 0) {
-    const bool map = build_tile_owner<1024>(mpre, E, omap);
-    build_tile_tables<1024>(jobs, soff, mpre, map ? omap : nullptr, E);
-  }
-  // wprefix written above by this workgroup is visible after the barrier.
-  // Four pairs per thread per round, their loads issued together; indices
-  // fit in 32 bits (T * k < 2^31).
-  const unsigned R = (unsigned)(T * k), uk = (unsigned)k;
-  for (unsigned p0 = tid; p0 < R; p0 += 4 * 1024) {
-    int e[4];
-    uint64_t word[4];
-    int32_t pre_b[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const unsigned p = p0 + u * 1024;
-      e[u] = p < R ? topk_idx[p] : -1;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const unsigned p = p0 + u * 1024;
-      const bool valid = p < R && e[u] >= 0 && e[u] < E;
-      const int64_t at = valid ? (int64_t)e[u] * W + ((p / uk) >> 6) : 0;
-      word[u] = valid ? mask[at] : 0ull;
-      pre_b[u] = valid ? wprefix[at] : 0;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const unsigned p = p0 + u * 1024;
-      if (p >= R) continue;
-      if (e[u] < 0 || e[u] >= E) {  // outside the contract; keep memory safe
-        pair_row[p] = -1;
-        continue;
-      }
-      const unsigned t = p / uk;
-      const uint64_t below = word[u] & ((1ull << (t & 63)) - 1ull);
-      const int32_t r = soff[e[u]] + pre_b[u] + __popcll(below);
-      row_token[r] = (int32_t)t;
-      pair_row[p] = r;
-    }
-  }
+  __shared__ PermuteLds<1024> L;
+  permute_core<1024>(topk_idx, T, k, E, mask, W, wprefix, counts, offsets, row_token, pair_row,
+                     jobs, L);
 }
+
 
 // x_perm[r] = x[row_token[r]], 16-byte chunks.
 __global__ __launch_bounds__(256) void k_gather_rows(const uint8_t* __restrict__ x,

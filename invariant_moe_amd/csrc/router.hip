@@ -7,45 +7,9 @@
 // expert (same DeepSeek-V4 page, section 6.3).
 #include "common.hpp"
 #include "kernels.hpp"
+#include "routing.hpp"
 
 namespace moe {
-
-// ---------------------------------------------------------------------------
-// Routing exp (fp32): Cody–Waite argument reduction x = n ln2 + r with
-// n = rint(x log2e) and ln2 split into fp32(ln2) + fp32(ln2 - fp32(ln2)),
-// then the degree-7 Taylor polynomial sum_{j<=7} r^j / j! with fp32-rounded
-// coefficients by Horner's rule with fused multiply-adds, then p * 2^n (two
-// exact power-of-two scalings outside [2^-126, 2^127]).  Written from the
-// mathematics; the routing keys depend on every bit of it.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ float pow2i(int m) {  // 2^m for -126 <= m <= 127
-  return __uint_as_float((uint32_t)(m + 127) << 23);
-}
-
-__device__ float routing_exp(float x) {
-  if (x != x) return x;
-  if (x > 89.0f) return __builtin_inff();
-  if (x < -104.0f) return 0.0f;
-  const float n = __builtin_rintf(x * 0x1.715476p+0f);
-  float r = __builtin_fmaf(-n, 0x1.62e430p-1f, x);
-  r = __builtin_fmaf(-n, -0x1.05c610p-29f, r);
-  float p = 0x1.a01a02p-13f;               // 1/7!
-  p = __builtin_fmaf(p, r, 0x1.6c16c2p-10f);  // 1/6!
-  p = __builtin_fmaf(p, r, 0x1.111112p-7f);   // 1/5!
-  p = __builtin_fmaf(p, r, 0x1.555556p-5f);   // 1/4!
-  p = __builtin_fmaf(p, r, 0x1.555556p-3f);   // 1/3!
-  p = __builtin_fmaf(p, r, 0.5f);
-  p = __builtin_fmaf(p, r, 1.0f);
-  p = __builtin_fmaf(p, r, 1.0f);
-  const int ni = (int)n;
-  if (ni > 127) return (p * pow2i(ni - 64)) * pow2i(64);
-  if (ni < -126) return (p * pow2i(ni + 64)) * pow2i(-64);
-  return p * pow2i(ni);
-}
-
-__device__ __forceinline__ float routing_sigmoid(float l) {
-  return 1.0f / (1.0f + routing_exp(-l));
-}
 
 // ---------------------------------------------------------------------------
 // Router logits.  One workgroup = TT tokens x (4 * EW) experts; wave w owns
@@ -84,7 +48,7 @@ __global__ __launch_bounds__(256) void k_router_logits(const ACT* __restrict__ x
                                                        int D, int E, float* __restrict__ logits,
                                                        unsigned long long* __restrict__ zero_words,
                                                        int64_t n_zero) {
-  // clear the (expert, token-block) words the top-k kernel ORs into
+  // clear words that a later kernel of the call counts into
   if (zero_words) {
     const int64_t nb = (int64_t)gridDim.x * gridDim.y;
     const int64_t b = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
@@ -184,100 +148,23 @@ __global__ __launch_bounds__(256) void k_router_logits(const ACT* __restrict__ x
 }
 
 // ---------------------------------------------------------------------------
-// Top-k, one wave per token, C = ceil(E/64) expert slots per lane.  Selection
-// key order: larger key first, then lower expert id; keys are compared as
-// floats (+0 == -0).  A NaN key is treated as -inf so the selection stays a
-// total order (inputs are required to be finite; this only keeps the kernel
-// memory-safe).  k rounds of a 64-lane butterfly arg-max; lane r keeps the
-// rank-r winner.  The weights' normaliser sums the selected terms in ascending
-// expert id.  With a mask, each selected (token, expert) sets bit t%64 of
-// word mask[e][t/64] (integer OR: order-free; the words were zeroed by the
-// logits kernel).
+// Top-k, one wave per token (topk_token in routing.hpp: a token's selection
+// is a long dependent chain, so tokens run side by side).  With a mask, each
+// selected (token, expert) sets bit t%64 of word mask[e][t/64] (integer OR:
+// order-free; the words were zeroed by the router-logits kernel).
 // ---------------------------------------------------------------------------
-struct Cand {
-  float key;
-  int id;  // -1 = none
-};
-
-__device__ __forceinline__ bool cand_better(const Cand& a, const Cand& b) {
-  if (a.id < 0) return false;
-  if (b.id < 0) return true;
-  return a.key > b.key || (a.key == b.key && a.id < b.id);
-}
-
 template <int C>
 __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits,
                                               const float* __restrict__ bias, int64_t T, int E,
                                               int k, int mode, int32_t* __restrict__ topk_idx,
                                               float* __restrict__ topk_w,
                                               unsigned long long* __restrict__ mask, int64_t W) {
-  const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // whole wave; no workgroup barriers below
-  float key[C], val[C];
-  uint32_t taken = 0;
-#pragma unroll
-  for (int c = 0; c < C; ++c) {
-    const int e = lane + 64 * c;
-    key[c] = 0.0f;
-    val[c] = 0.0f;
-    if (e < E) {
-      const float l = logits[t * E + e];
-      const float sc = (mode == MOE_ROUTE_SIGMOID) ? routing_sigmoid(l) : l;
-      float kk = bias ? sc + bias[e] : sc;
-      if (kk != kk) kk = -__builtin_inff();
-      key[c] = kk;
-      val[c] = sc;
-    } else {
-      taken |= 1u << c;
-    }
-  }
-  int my_id = 0;
-  float my_val = 0.0f;
-  for (int r = 0; r < k; ++r) {
-    Cand best{0.0f, -1};
-#pragma unroll
-    for (int c = 0; c < C; ++c) {
-      Cand cc{key[c], ((taken >> c) & 1u) ? -1 : lane + 64 * c};
-      if (cand_better(cc, best)) best = cc;
-    }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      Cand o{__shfl_xor(best.key, m), __shfl_xor(best.id, m)};
-      if (cand_better(o, best)) best = o;
-    }
-    const int win = best.id < 0 ? 0 : best.id;  // k <= E: always a winner
-    const int owner = win & 63;
-    float ov = 0.0f;
-    if (lane == owner) {
-      taken |= 1u << (win >> 6);
-#pragma unroll
-      for (int c = 0; c < C; ++c)
-        if (c == (win >> 6)) ov = val[c];
-    }
-    ov = __shfl(ov, owner);
-    if (lane == r) {
-      my_id = win;
-      my_val = ov;
-    }
-  }
-  const float top = __shfl(my_val, 0);
-  const bool act = lane < k;
-  const float z = !act ? 0.0f
-                       : (mode == MOE_ROUTE_SOFTMAX ? routing_exp(my_val - top) : my_val);
-  int pos = 0;  // rank of this slot by ascending expert id
-  for (int q = 0; q < k; ++q) pos += (__shfl(my_id, q) < my_id) ? 1 : 0;
-  float Z = 0.0f;
-  for (int i = 0; i < k; ++i) {
-    const unsigned long long b = __ballot(act && pos == i);
-    const int src = b ? __builtin_ctzll(b) : 0;
-    Z = Z + __shfl(z, src);
-  }
-  if (act) {
-    topk_idx[t * k + lane] = my_id;
-    topk_w[t * k + lane] = z / Z;
-    if (mask) atomicOr(&mask[(int64_t)my_id * W + (t >> 6)], 1ull << (t & 63));
-  }
+  int my_id;
+  if (topk_token<C>(logits + t * E, bias, E, k, mode, topk_idx + t * k, topk_w + t * k, my_id) &&
+      mask)
+    atomicOr(&mask[(int64_t)my_id * W + (t >> 6)], 1ull << (t & 63));
 }
 
 // ---------------------------------------------------------------------------
@@ -356,10 +243,10 @@ static void launch_logits_cfg(const void* x, int act, const void* w, int64_t T, 
 }
 
 hipError_t launch_router_logits(const void* x, int act, const void* w, int64_t T, int D, int E,
-                                float* logits, uint64_t* zero_mask, hipStream_t s) {
+                                float* logits, uint64_t* zero, int64_t n_zero, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  unsigned long long* zw = reinterpret_cast<unsigned long long*>(zero_mask);
-  const int64_t nz = zero_mask ? (int64_t)E * ((T + 63) / 64) : 0;
+  unsigned long long* zw = reinterpret_cast<unsigned long long*>(zero);
+  const int64_t nz = zero ? n_zero : 0;
   // Tile choice only changes how many (token, expert) pairs a workgroup holds
   // (enough workgroups to stream the router weights); every pair's logit is
   // the same fixed chain.
