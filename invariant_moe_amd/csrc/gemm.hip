@@ -652,7 +652,7 @@ __global__ __launch_bounds__(1024) void k_tile_tables(const int32_t* __restrict_
   __syncthreads();
   tile_scan2<1024>(mpre, unused, E, wsum);
   const bool map = build_tile_owner<1024>(mpre, E, omap);
-  build_tile_tables<1024>(jobs, soff, mpre, map ? omap : nullptr, E);
+  build_tile_tables<1024>(jobs, soff, mpre, map ? omap : nullptr, E, 0, 1);
 }
 
 hipError_t launch_tile_tables(const int32_t* offsets, int E, const TileJobs& jobs, hipStream_t s) {

@@ -47,7 +47,7 @@ __global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ to
                                                   TileJobs jobs) {
   __shared__ PermuteLds<1024> L;
   permute_core<1024>(topk_idx, T, k, E, mask, W, wprefix, counts, offsets, row_token, pair_row,
-                     jobs, L);
+                     jobs, L, blockIdx.x, gridDim.x);
 }
 
 
@@ -82,8 +82,16 @@ hipError_t launch_permute(const int32_t* topk_idx, int64_t T, int k, int E, cons
                           int32_t* pair_row, const TileJobs* jobs, hipStream_t s) {
   const int64_t W = (T + 63) / 64;
   TileJobs none{};
-  hipLaunchKernelGGL(k_permute, dim3(1), dim3(1024), 0, s, topk_idx, T, k, E, mask, W, wprefix,
-                     counts, offsets, row_token, pair_row, jobs ? *jobs : none);
+  // Workgroups: enough that each scatters at most 4 pairs and writes at most
+  // two table entries per thread (each repeats the cheap counting and scans).
+  int64_t entries = 0;
+  if (jobs)
+    for (int j = 0; j < jobs->n; ++j) entries += jobs->job[j].grid;
+  int64_t nwg = (T * k + 4095) / 4096;
+  if ((entries + 2047) / 2048 > nwg) nwg = (entries + 2047) / 2048;
+  nwg = nwg < 1 ? 1 : (nwg > 32 ? 32 : nwg);
+  hipLaunchKernelGGL(k_permute, dim3((unsigned)nwg), dim3(1024), 0, s, topk_idx, T, k, E, mask, W,
+                     wprefix, counts, offsets, row_token, pair_row, jobs ? *jobs : none);
   return hipGetLastError();
 }
 

@@ -49,24 +49,42 @@ __device__ __forceinline__ float routing_sigmoid(float l) {
 }
 
 // ---------------------------------------------------------------------------
-// Top-k of one token by one wave, C = ceil(E/64) expert slots per lane.
-// Selection key order: larger key first, then lower expert id; keys are
-// compared as floats (+0 == -0).  A NaN key is treated as -inf so the
-// selection stays a total order (inputs are required to be finite; this only
-// keeps the kernel memory-safe).  k rounds of a 64-lane butterfly arg-max;
-// lane r keeps the rank-r winner.  The weights' normaliser sums the selected
-// terms in ascending expert id.  Writes idx[0..k) and w[0..k) of the token;
-// lanes r < k return their expert in my_id and true.
+// Top-k of one token by one wave, C = ceil(E/64) expert slots per lane
+// (expert e = lane + 64 c).  Selection order: larger key first, then lower
+// expert id; keys compare as floats (+0 == -0).  A NaN key is treated as -inf
+// so the selection stays a total order (inputs are required to be finite;
+// this only keeps the kernel memory-safe).  Round r picks the best key not
+// yet taken: keys are mapped to order-preserving uint32 codes, the wave
+// maximum comes from four DPP steps within each row of 16 lanes and a scalar
+// maximum over the four rows, and the winner is the lowest expert id holding
+// that code (ballots in ascending id order).  Lane r keeps the rank-r winner.
+// The weights' normaliser sums the selected terms in ascending expert id.
+// Writes idx[0..k) and w[0..k) of the token; lanes r < k return their expert
+// in my_id and true.
 // ---------------------------------------------------------------------------
-struct Cand {
-  float key;
-  int id;  // -1 = none
-};
+__device__ __forceinline__ uint32_t key_code(float kk) {
+  if (kk == 0.0f) kk = 0.0f;  // -0 -> +0
+  const uint32_t u = __float_as_uint(kk);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);  // > 0 for every non-NaN key
+}
 
-__device__ __forceinline__ bool cand_better(const Cand& a, const Cand& b) {
-  if (a.id < 0) return false;
-  if (b.id < 0) return true;
-  return a.key > b.key || (a.key == b.key && a.id < b.id);
+__device__ __forceinline__ uint32_t umax32(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+// Maximum over the 64 lanes, returned uniform (scalar).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = umax32(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]
+  v = umax32(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));   // quad [2,3,0,1]
+  v = umax32(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));  // half-row mirror
+  v = umax32(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));  // row mirror
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return umax32(umax32(r0, r1), umax32(r2, r3));
+}
+
+__device__ __forceinline__ float readlane_f32(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
 // Raw loads of one token's logits (lane + 64 c) and of the bias, kept apart
@@ -87,64 +105,60 @@ __device__ __forceinline__ bool topk_select(const float (&raw)[C], const float (
                                             int32_t* __restrict__ idx, float* __restrict__ w,
                                             int& my_id_out) {
   const int lane = threadIdx.x & 63;
-  float key[C], val[C];
-  uint32_t taken = 0;
+  uint32_t code[C];  // 0 = no expert / already taken
+  float val[C];
 #pragma unroll
   for (int c = 0; c < C; ++c) {
     const int e = lane + 64 * c;
-    key[c] = 0.0f;
+    code[c] = 0u;
     val[c] = 0.0f;
     if (e < E) {
       const float l = raw[c];
       const float sc = (mode == MOE_ROUTE_SIGMOID) ? routing_sigmoid(l) : l;
       float kk = has_bias ? sc + bias_v[c] : sc;
       if (kk != kk) kk = -__builtin_inff();
-      key[c] = kk;
+      code[c] = key_code(kk);
       val[c] = sc;
-    } else {
-      taken |= 1u << c;
     }
   }
   int my_id = 0;
   float my_val = 0.0f;
   for (int r = 0; r < k; ++r) {
-    Cand best{0.0f, -1};
+    uint32_t best = code[0];
 #pragma unroll
-    for (int c = 0; c < C; ++c) {
-      Cand cc{key[c], ((taken >> c) & 1u) ? -1 : lane + 64 * c};
-      if (cand_better(cc, best)) best = cc;
-    }
+    for (int c = 1; c < C; ++c) best = umax32(best, code[c]);
+    const uint32_t m = wave_max_u32(best);
+    int win = 0;  // k <= E: some expert holds the maximum
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      Cand o{__shfl_xor(best.key, m), __shfl_xor(best.id, m)};
-      if (cand_better(o, best)) best = o;
+    for (int c = C - 1; c >= 0; --c) {  // the lowest slot with a hit wins
+      const unsigned long long hit = __ballot(code[c] == m);
+      if (hit) win = 64 * c + __builtin_ctzll(hit);
     }
-    const int win = best.id < 0 ? 0 : best.id;  // k <= E: always a winner
-    const int owner = win & 63;
+    const int owner = win & 63, wc = win >> 6;
     float ov = 0.0f;
-    if (lane == owner) {
-      taken |= 1u << (win >> 6);
 #pragma unroll
-      for (int c = 0; c < C; ++c)
-        if (c == (win >> 6)) ov = val[c];
-    }
-    ov = __shfl(ov, owner);
+    for (int c = 0; c < C; ++c)
+      if (c == wc) {
+        ov = val[c];
+        if (lane == owner) code[c] = 0u;
+      }
+    ov = readlane_f32(ov, owner);
     if (lane == r) {
       my_id = win;
       my_val = ov;
     }
   }
-  const float top = __shfl(my_val, 0);
+  const float top = readlane_f32(my_val, 0);
   const bool act = lane < k;
   const float z = !act ? 0.0f
                        : (mode == MOE_ROUTE_SOFTMAX ? routing_exp(my_val - top) : my_val);
   int pos = 0;  // rank of this slot by ascending expert id
-  for (int q = 0; q < k; ++q) pos += (__shfl(my_id, q) < my_id) ? 1 : 0;
+  for (int q = 0; q < k; ++q) pos += (__builtin_amdgcn_readlane(my_id, q) < my_id) ? 1 : 0;
   float Z = 0.0f;
   for (int i = 0; i < k; ++i) {
     const unsigned long long b = __ballot(act && pos == i);
     const int src = b ? __builtin_ctzll(b) : 0;
-    Z = Z + __shfl(z, src);
+    Z = Z + readlane_f32(z, src);
   }
   if (act) {
     idx[lane] = my_id;

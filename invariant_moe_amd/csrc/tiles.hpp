@@ -90,8 +90,8 @@ __device__ bool build_tile_owner(const int* mpre, int E, int* omap) {
   return fits;
 }
 
-// One workgroup of NT threads writes every job's table, one entry per thread
-// per round in table order (coalesced stores).  soff: exclusive group offsets
+// Workgroup wg of nwg (NT threads each) writes entries wg*NT + tid, stepping
+// by nwg*NT, of every job's table, in table order (coalesced stores).  soff: exclusive group offsets
 // [E+1]; mpre: exclusive prefix [E+1] of ceil(rows_e / jobs.BM); omap: owner
 // map or nullptr.  Tiles of a grouped segment are numbered group-major, then
 // by feature tile, then by row tile, so tile li lies in the group whose row
@@ -100,7 +100,7 @@ __device__ bool build_tile_owner(const int* mpre, int E, int* omap) {
 // more workgroups).
 template <int NT>
 __device__ void build_tile_tables(const TileJobs& jobs, const int* soff, const int* mpre,
-                                  const int* omap, int E) {
+                                  const int* omap, int E, int wg, int nwg) {
   const int BM = jobs.BM;
 #pragma unroll 1
   for (int j = 0; j < jobs.n; ++j) {  // uniform: job fields come from scalar loads
@@ -115,7 +115,7 @@ __device__ void build_tile_tables(const TileJobs& jobs, const int* soff, const i
     }
     const int total = tot[0] + tot[1];
     const unsigned chunk = (unsigned)(total + 7) / 8u;
-    for (int b = threadIdx.x; b < grid; b += NT) {
+    for (int b = wg * NT + threadIdx.x; b < grid; b += nwg * NT) {
       int4 d = make_int4(0, 0, 0, 0);
       const unsigned q = (unsigned)b / 8u;
       const unsigned l = ((unsigned)b % 8u) * chunk + q;
