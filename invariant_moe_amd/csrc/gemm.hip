@@ -65,28 +65,22 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 }
 
 // Exact decode of 32 E2M1 codes (16 bytes, element 2i in the low nibble of
-// byte i) with one E8M0 scale byte into 32 bf16 values.  The product code *
-// 2^(s-127) has at most two significant bits, so it is exact in bf16 for every
-// scale byte <= 252.
+// byte i) with one E8M0 scale byte into 32 bf16 values, by gfx950's scaled
+// conversion (two codes times an fp32 scale to two bf16 per instruction).  The
+// scale 2^(s-127) is built exactly in fp32 (subnormal for s = 0; s = 255 is
+// the E8M0 NaN and gives NaN weights).  Every product code * 2^(s-127) has at
+// most two significant bits, so it is exact in bf16 (subnormals included)
+// unless it overflows; checked on MI355X against the bit-level decode for all
+// 256 x 256 (scale, code byte) pairs.
 __device__ __forceinline__ void decode_mxfp4_32(const uint4 q, uint32_t sbyte, uint32_t (&o)[16]) {
   const float scale = sbyte ? __uint_as_float(sbyte << 23) : __uint_as_float(0x00400000u);
   const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const uint32_t byte = (w[i] >> (8 * b)) & 0xffu;
-      uint32_t pair = 0;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t c = (byte >> (4 * h)) & 0xfu;
-        const uint32_t m = c & 7u;
-        const uint32_t mag = m >= 2u ? ((m << 22) + 0x3f000000u) : (m ? 0x3f000000u : 0u);
-        const uint32_t v = __float_as_uint(__uint_as_float(mag) * scale);  // exact
-        pair |= ((v >> 16) | ((c & 8u) << 12)) << (16 * h);
-      }
-      o[i * 4 + b] = pair;
-    }
+    o[i * 4 + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scale, 0));
+    o[i * 4 + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scale, 1));
+    o[i * 4 + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scale, 2));
+    o[i * 4 + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scale, 3));
   }
 }
 
