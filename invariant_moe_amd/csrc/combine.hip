@@ -42,6 +42,7 @@ struct Row8<float> {
 
 // TPT threads per token (a power of two covering D/8, at most 256), 256/TPT
 // tokens per workgroup; each thread owns 8 consecutive features per pass.
+// Wide rows are split over gridDim.y workgroups (one pass per thread).
 template <typename ACT>
 __global__ __launch_bounds__(256) void k_combine(const ACT* __restrict__ eo,
                                                  const int32_t* __restrict__ topk_idx,
@@ -72,7 +73,7 @@ __global__ __launch_bounds__(256) void k_combine(const ACT* __restrict__ eo,
   }
   __syncthreads();
   if (t >= T) return;
-  for (int d = lt * 8; d < D; d += TPT * 8) {
+  for (int d = (blockIdx.y * TPT + lt) * 8; d < D; d += gridDim.y * TPT * 8) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int q = 0; q < k; ++q) {
       float v[8];
@@ -97,13 +98,13 @@ hipError_t launch_combine(const void* eo, const int32_t* topk_idx, const float* 
   if (T == 0) return hipSuccess;
   int tpt = 64;  // >= k (k <= 32) so the slot setup fits in one token's threads
   while (tpt < 256 && tpt * 8 < D) tpt *= 2;
-  const unsigned grid = (unsigned)((T + (256 / tpt) - 1) / (256 / tpt));
+  const dim3 grid((unsigned)((T + (256 / tpt) - 1) / (256 / tpt)),
+                   (unsigned)((D / 8 + tpt - 1) / tpt));
   if (act == MOE_BF16)
-    hipLaunchKernelGGL(k_combine<uint16_t>, dim3(grid), dim3(256), 0, s, (const uint16_t*)eo,
-                       topk_idx, topk_w, pair_row, (const uint16_t*)shared, T, k, D, tpt,
-                       (uint16_t*)y);
+    hipLaunchKernelGGL(k_combine<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)eo, topk_idx,
+                       topk_w, pair_row, (const uint16_t*)shared, T, k, D, tpt, (uint16_t*)y);
   else
-    hipLaunchKernelGGL(k_combine<float>, dim3(grid), dim3(256), 0, s, (const float*)eo, topk_idx,
+    hipLaunchKernelGGL(k_combine<float>, grid, dim3(256), 0, s, (const float*)eo, topk_idx,
                        topk_w, pair_row, (const float*)shared, T, k, D, tpt, (float*)y);
   return hipGetLastError();
 }

@@ -456,6 +456,11 @@ enum TileCfg {
   TILE_64x128_2x2_P2,
   TILE_64x64_4x1_P3,
   TILE_128x64_4x1_P2,
+  TILE_16x32_1x2_P8,
+  TILE_16x64_1x4_P8,
+  TILE_16x32_1x2_P6,
+  TILE_16x64_1x4_P6,
+  TILE_16x16_1x1_P8,
   TILE_COUNT,
   TILE_F32 = 100        // fp32 VALU kernel, 16 x 16 tiles
 };
@@ -491,6 +496,11 @@ static TileShape tile_shape(int cfg) {
     case TILE_64x128_2x2_P2: return {64, 128};
     case TILE_64x64_4x1_P3: return {64, 64};
     case TILE_128x64_4x1_P2: return {128, 64};
+    case TILE_16x32_1x2_P8: return {16, 32};
+    case TILE_16x64_1x4_P8: return {16, 64};
+    case TILE_16x32_1x2_P6: return {16, 32};
+    case TILE_16x64_1x4_P6: return {16, 64};
+    case TILE_16x16_1x1_P8: return {16, 16};
     default: return {16, 16};  // TILE_F32
   }
 }
@@ -524,6 +534,11 @@ static hipError_t launch_tile_cfg(int cfg, const GemmArgs& a, bool gated, int64_
     case TILE_64x128_2x2_P2: return launch_one<64, 128, 2, 2, 2, FP4>(a, gated, grid, st, ev);
     case TILE_64x64_4x1_P3: return launch_one<64, 64, 4, 1, 3, FP4>(a, gated, grid, st, ev);
     case TILE_128x64_4x1_P2: return launch_one<128, 64, 4, 1, 2, FP4>(a, gated, grid, st, ev);
+    case TILE_16x32_1x2_P8: return launch_one<16, 32, 1, 2, 8, FP4>(a, gated, grid, st, ev);
+    case TILE_16x64_1x4_P8: return launch_one<16, 64, 1, 4, 8, FP4>(a, gated, grid, st, ev);
+    case TILE_16x32_1x2_P6: return launch_one<16, 32, 1, 2, 6, FP4>(a, gated, grid, st, ev);
+    case TILE_16x64_1x4_P6: return launch_one<16, 64, 1, 4, 6, FP4>(a, gated, grid, st, ev);
+    case TILE_16x16_1x1_P8: return launch_one<16, 16, 1, 1, 8, FP4>(a, gated, grid, st, ev);
     default: return hipErrorInvalidValue;
   }
 }

@@ -42,6 +42,40 @@ struct ActIO<float> {
   }
 };
 
+// Fixed-tree reduction of the 64 partials of each (token, expert) pair of a
+// wave, 32 pairs per round: partial[j] += partial[j + m], m = 32..1, by one
+// lane per pair after a transpose through LDS.  Element (pair q, partial j)
+// sits at q*64 + (j ^ q) so that both the write (fixed q, lanes j) and the
+// read (lanes q, fixed j) hit distinct banks.  myred: this wave's 32*64 floats.
+template <int TT, int EW>
+__device__ __forceinline__ void logits_tree_store(const float (&acc)[TT][EW], float* myred,
+                                                  int64_t t0, int ew0, int64_t T, int E,
+                                                  float* __restrict__ logits) {
+  constexpr int NP = TT * EW;
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int base = 0; base < NP; base += 32) {
+    __syncthreads();
+#pragma unroll
+    for (int q = base; q < NP && q < base + 32; ++q)
+      myred[(q - base) * 64 + (lane ^ (q - base))] = acc[q / EW][q % EW];
+    __syncthreads();
+    const int q = base + lane;
+    if (lane < 32 && q < NP) {
+      float p[64];
+#pragma unroll
+      for (int j = 0; j < 64; ++j) p[j] = myred[lane * 64 + (j ^ lane)];
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1)
+#pragma unroll
+        for (int j = 0; j < m; ++j) p[j] = p[j] + p[j + m];
+      const int64_t t = t0 + q / EW;
+      const int e = ew0 + q % EW;
+      if (t < T && e < E) logits[t * E + e] = p[0];
+    }
+  }
+}
+
 template <typename ACT, int TT, int EW>
 __global__ __launch_bounds__(256) void k_router_logits(const ACT* __restrict__ x,
                                                        const ACT* __restrict__ w, int64_t T,
@@ -54,7 +88,6 @@ __global__ __launch_bounds__(256) void k_router_logits(const ACT* __restrict__ x
     const int64_t b = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
     for (int64_t i = b * 256 + threadIdx.x; i < n_zero; i += nb * 256) zero_words[i] = 0ull;
   }
-  constexpr int NP = TT * EW;  // pairs per wave
   constexpr int XS_BYTES = TT * 512 * (int)sizeof(ACT);
   constexpr int RED_BYTES = 4 * 32 * 64 * 4;
   constexpr int SMEM = XS_BYTES > RED_BYTES ? XS_BYTES : RED_BYTES;
@@ -120,31 +153,103 @@ __global__ __launch_bounds__(256) void k_router_logits(const ACT* __restrict__ x
     }
   }
 
-  // Fixed-tree reduction of the 64 partials of each pair, 32 pairs per round.
-  // Element (pair q, partial j) sits at q*64 + (j ^ q) so that both the
-  // write (fixed q, lanes j) and the read (lanes q, fixed j) hit distinct banks.
-  float* myred = red + wave * 32 * 64;
+  logits_tree_store<TT, EW>(acc, red + wave * 32 * 64, t0, ew0, T, E, logits);
+}
+
+// x and w chunks of one 512-wide step, loaded straight into registers
+// (small T): lane j reads elements 8j .. 8j+7 of the step.
+template <typename ACT>
+struct Chunk8;
+template <>
+struct Chunk8<uint16_t> {  // 8 bf16
+  uint4 q;
+  __device__ void load(const uint16_t* p) { q = *reinterpret_cast<const uint4*>(p); }
+  __device__ void unpack(float (&v)[8]) const {
+    v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x);
+    v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
+    v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z);
+    v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
+  }
+};
+template <>
+struct Chunk8<float> {  // 8 fp32
+  float4 a, b;
+  __device__ void load(const float* p) {
+    a = reinterpret_cast<const float4*>(p)[0];
+    b = reinterpret_cast<const float4*>(p)[1];
+  }
+  __device__ void unpack(float (&v)[8]) const {
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+};
+
+// Router logits for small T: the same pairs, partials and order as above, but
+// every lane reads its x and w chunks from global memory into a register ring
+// P steps deep (loads of step i+P are issued before step i is summed), with
+// no LDS staging and no barrier in the loop.  Out-of-range rows, experts and
+// the tail of D are read at clamped addresses and never summed.
+template <typename ACT, int TT, int EW, int P>
+__global__ __launch_bounds__(256) void k_router_logits_small(
+    const ACT* __restrict__ x, const ACT* __restrict__ w, int64_t T, int D, int E,
+    float* __restrict__ logits, unsigned long long* __restrict__ zero_words, int64_t n_zero) {
+  if (zero_words) {
+    const int64_t nb = (int64_t)gridDim.x * gridDim.y;
+    const int64_t b = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+    for (int64_t i = b * 256 + threadIdx.x; i < n_zero; i += nb * 256) zero_words[i] = 0ull;
+  }
+  __shared__ __align__(16) float red[4 * 32 * 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t t0 = (int64_t)blockIdx.x * TT;
+  const int ew0 = blockIdx.y * 4 * EW + wave * EW;
+  const int NI = (D + 511) / 512;
+  const ACT* xrow[TT];
+  const ACT* wrow[EW];
 #pragma unroll
-  for (int base = 0; base < NP; base += 32) {
-    __syncthreads();
+  for (int t = 0; t < TT; ++t) xrow[t] = x + (t0 + t < T ? t0 + t : T - 1) * (int64_t)D;
 #pragma unroll
-    for (int q = base; q < NP && q < base + 32; ++q)
-      myred[(q - base) * 64 + (lane ^ (q - base))] = acc[q / EW][q % EW];
-    __syncthreads();
-    const int q = base + lane;
-    if (lane < 32 && q < NP) {
-      float p[64];
+  for (int e = 0; e < EW; ++e) wrow[e] = w + (int64_t)(ew0 + e < E ? ew0 + e : E - 1) * D;
+
+  float acc[TT][EW];
 #pragma unroll
-      for (int j = 0; j < 64; ++j) p[j] = myred[lane * 64 + (j ^ lane)];
+  for (int t = 0; t < TT; ++t)
 #pragma unroll
-      for (int m = 32; m >= 1; m >>= 1)
+    for (int e = 0; e < EW; ++e) acc[t][e] = 0.0f;
+
+  Chunk8<ACT> xr[P][TT], wr[P][EW];
+  auto load = [&](int q, int i) {
+    const int d = min(i * 512 + 8 * lane, D - 8);
 #pragma unroll
-        for (int j = 0; j < m; ++j) p[j] = p[j] + p[j + m];
-      const int64_t t = t0 + q / EW;
-      const int e = ew0 + q % EW;
-      if (t < T && e < E) logits[t * E + e] = p[0];
+    for (int t = 0; t < TT; ++t) xr[q][t].load(xrow[t] + d);
+#pragma unroll
+    for (int e = 0; e < EW; ++e) wr[q][e].load(wrow[e] + d);
+  };
+#pragma unroll
+  for (int q = 0; q < P; ++q) load(q, min(q, NI - 1));
+  for (int i0 = 0; i0 < NI; i0 += P) {
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+      const int i = i0 + q;
+      if (i < NI) {  // uniform
+        if (i * 512 + 8 * lane < D) {
+          float wv[EW][8];
+#pragma unroll
+          for (int e = 0; e < EW; ++e) wr[q][e].unpack(wv[e]);
+#pragma unroll
+          for (int t = 0; t < TT; ++t) {
+            float xv[8];
+            xr[q][t].unpack(xv);
+#pragma unroll
+            for (int e = 0; e < EW; ++e)
+#pragma unroll
+              for (int c = 0; c < 8; ++c) acc[t][e] = __builtin_fmaf(xv[c], wv[e][c], acc[t][e]);
+          }
+        }
+        load(q, min(i + P, NI - 1));
+      }
     }
   }
+  logits_tree_store<TT, EW>(acc, red + wave * 32 * 64, t0, ew0, T, E, logits);
 }
 
 // ---------------------------------------------------------------------------
@@ -242,20 +347,32 @@ static void launch_logits_cfg(const void* x, int act, const void* w, int64_t T, 
                        (const float*)w, T, D, E, logits, zw, nz);
 }
 
+template <int TT, int EW, int P>
+static void launch_logits_small(const void* x, int act, const void* w, int64_t T, int D, int E,
+                                float* logits, unsigned long long* zw, int64_t nz,
+                                hipStream_t s) {
+  dim3 grid((unsigned)((T + TT - 1) / TT), (unsigned)((E + 4 * EW - 1) / (4 * EW)));
+  if (act == MOE_BF16)
+    hipLaunchKernelGGL((k_router_logits_small<uint16_t, TT, EW, P>), grid, dim3(256), 0, s,
+                       (const uint16_t*)x, (const uint16_t*)w, T, D, E, logits, zw, nz);
+  else
+    hipLaunchKernelGGL((k_router_logits_small<float, TT, EW, P>), grid, dim3(256), 0, s,
+                       (const float*)x, (const float*)w, T, D, E, logits, zw, nz);
+}
+
 hipError_t launch_router_logits(const void* x, int act, const void* w, int64_t T, int D, int E,
                                 float* logits, uint64_t* zero, int64_t n_zero, hipStream_t s) {
   if (T == 0) return hipSuccess;
   unsigned long long* zw = reinterpret_cast<unsigned long long*>(zero);
   const int64_t nz = zero ? n_zero : 0;
   // Tile choice only changes how many (token, expert) pairs a workgroup holds
-  // (enough workgroups to stream the router weights); every pair's logit is
-  // the same fixed chain.
+  // and how x reaches the lanes; every pair's logit is the same fixed chain.
   if (((T + 15) / 16) * ((E + 31) / 32) >= 512)
     launch_logits_cfg<16, 8>(x, act, w, T, D, E, logits, zw, nz, s);
   else if (T >= 8)
-    launch_logits_cfg<4, 2>(x, act, w, T, D, E, logits, zw, nz, s);
+    launch_logits_small<4, 2, 4>(x, act, w, T, D, E, logits, zw, nz, s);
   else
-    launch_logits_cfg<1, 1>(x, act, w, T, D, E, logits, zw, nz, s);
+    launch_logits_small<1, 1, 8>(x, act, w, T, D, E, logits, zw, nz, s);
   return hipGetLastError();
 }
 
