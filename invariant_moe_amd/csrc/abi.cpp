@@ -70,18 +70,22 @@ FfnPlans ffn_plans(int64_t R, int64_t T, int D, int E, int I, int Is, moe_dtype 
   return p;
 }
 
-// Tile-table entries reserved for a layer: the larger of the one-launch and
-// the per-format (two-launch) plans, so the size does not depend on the
-// weight formats.
-int64_t layer_table_entries(int64_t T, int D, int E, int k, int I, int Is, moe_dtype act) {
-  const int64_t R = T * k;
+// Tile-table entries reserved for the two GEMMs: the largest over the weight
+// formats of the routed and shared experts (the formats change the launches
+// and tile shapes), so the workspace size does not depend on them.
+int64_t ffn_table_entries(int64_t R, int64_t T, int D, int E, int I, int Is, moe_dtype act) {
   int64_t n = 0;
-  for (int split = 0; split < 2; ++split) {
-    const FfnPlans p = ffn_plans(R, T, D, E, I, Is, act, 0, split);
-    const int64_t m = moe::plan_table_entries(p.up) + moe::plan_table_entries(p.dn);
-    n = m > n ? m : n;
-  }
+  for (int rf = 0; rf < 2; ++rf)
+    for (int sf = 0; sf < 2; ++sf) {
+      const FfnPlans p = ffn_plans(R, T, D, E, I, Is, act, rf, sf);
+      const int64_t m = moe::plan_table_entries(p.up) + moe::plan_table_entries(p.dn);
+      n = m > n ? m : n;
+    }
   return n;
+}
+
+int64_t layer_table_entries(int64_t T, int D, int E, int k, int I, int Is, moe_dtype act) {
+  return ffn_table_entries(T * k, T, D, E, I, Is, act);
 }
 
 struct LayerLayout {
@@ -304,10 +308,9 @@ int moe_permute(const int32_t* topk_idx, int64_t T, int k, int E, int32_t* exper
 size_t moe_grouped_swiglu_workspace_bytes(int64_t R, int E, int D, int I, moe_dtype act) {
   if (R <= 0 || E <= 0 || D <= 0 || I <= 0) return 0;
   const moe_dtype a = act == MOE_F32 ? MOE_F32 : MOE_BF16;
-  const FfnPlans p = ffn_plans(R, 0, D, E, I, 0, a, 0, 0);
   Carver c;
   c.take((size_t)R * I * act_size(a));
-  c.take((size_t)(moe::plan_table_entries(p.up) + moe::plan_table_entries(p.dn)) * sizeof(int4));
+  c.take((size_t)ffn_table_entries(R, 0, D, E, I, 0, a) * sizeof(int4));
   return c.off;
 }
 
@@ -333,6 +336,9 @@ int moe_grouped_swiglu(const void* x_rows, const int32_t* row_index, const int32
   hipStream_t s = static_cast<hipStream_t>(stream);
   const FfnPlans p = ffn_plans(R, 0, D, E, I, 0, act, w->dtype == MOE_MXFP4 ? 1 : 0, 0);
   if (!p.up.valid || !p.dn.valid) return fail(MOE_ERR_SHAPE, "problem too large for one launch");
+  if (moe::plan_table_entries(p.up) + moe::plan_table_entries(p.dn) >
+      ffn_table_entries(R, 0, D, E, I, 0, act))
+    return fail(MOE_ERR_WORKSPACE, "tile tables exceed their workspace region");
   Carver c;
   c.take((size_t)R * I * act_size(act));
   int4* tiles_up = reinterpret_cast<int4*>(static_cast<char*>(workspace) + c.off);

@@ -367,8 +367,12 @@ hipError_t launch_router_logits(const void* x, int act, const void* w, int64_t T
   const int64_t nz = zero ? n_zero : 0;
   // Tile choice only changes how many (token, expert) pairs a workgroup holds
   // and how x reaches the lanes; every pair's logit is the same fixed chain.
+  // Small T (decode): register ring, latency bound.  Larger T: x staged
+  // through LDS once per workgroup (measured faster from a few hundred tokens).
   if (((T + 15) / 16) * ((E + 31) / 32) >= 512)
     launch_logits_cfg<16, 8>(x, act, w, T, D, E, logits, zw, nz, s);
+  else if (T > 128)
+    launch_logits_cfg<4, 2>(x, act, w, T, D, E, logits, zw, nz, s);
   else if (T >= 8)
     launch_logits_small<4, 2, 4>(x, act, w, T, D, E, logits, zw, nz, s);
   else
