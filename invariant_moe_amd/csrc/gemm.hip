@@ -767,9 +767,12 @@ static hipError_t launch_tile_cfg(int cfg, const GemmArgs& a, bool gated, int64_
 
 // Host-side choice from the average rows per group (no device sync), from
 // measured sweeps on MI355X (all choices give identical bits).
-static int pick_tile_cfg(bool gated, int64_t rows_per_group_hint) {
+static int pick_tile_cfg(bool gated, int64_t rows_per_group_hint, bool fp4) {
   if (rows_per_group_hint <= 2) return gated ? TILE_16x32_1x2 : TILE_16x64_1x4;
   if (rows_per_group_hint <= 16) return TILE_32x64_1x4;
+  // MXFP4 weights: the decode in the LDS staging favours 128-row tiles
+  // (each decoded weight serves more token rows)
+  if (fp4 && rows_per_group_hint <= 96) return gated ? TILE_128x64_2x2 : TILE_128x128_2x2_P2;
   if (rows_per_group_hint <= 96) return gated ? TILE_64x32_4x1_P2 : TILE_64x64_4x1_P2;
   return TILE_128x128_2x2_P2;  // many rows per expert: the largest tile that fits
 }
@@ -782,7 +785,8 @@ GemmPlan plan_grouped_gemm(const SegShape* segs, int nseg, bool gated, int act,
   p.act = act;
   p.nseg = nseg;
   for (int i = 0; i < nseg; ++i) p.seg[i] = segs[i];
-  const int cfg = act == MOE_F32 ? (int)TILE_F32 : pick_tile_cfg(gated, rows_per_group_hint);
+  const int cfg = act == MOE_F32 ? (int)TILE_F32
+                                  : pick_tile_cfg(gated, rows_per_group_hint, segs[0].wfmt != 0);
   const TileShape ts = tile_shape(cfg);
   // Segments with the same weight format share one launch; a mixed pair
   // (MXFP4 routed experts + bf16 shared expert) takes one launch per format.

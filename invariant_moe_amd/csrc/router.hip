@@ -5,6 +5,8 @@
 // section 6.3; the "V4" article, section 2.2, describes the router as a small
 // linear layer giving E logits).  Hash routing maps hash(token id) mod E to an
 // expert (same DeepSeek-V4 page, section 6.3).
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "routing.hpp"
@@ -37,6 +39,41 @@ struct ActIO<float> {
   __device__ static void load8(const float* p, float (&v)[8]) {
     const float4 a = *reinterpret_cast<const float4*>(p);
     const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+};
+
+// x and w chunks of one 512-wide step, loaded straight into registers
+// (small T): lane j reads elements 8j .. 8j+7 of the step.
+template <typename ACT>
+struct Chunk8;
+template <>
+struct Chunk8<uint16_t> {  // 8 bf16
+  uint4 q;
+  __device__ void load(const uint16_t* p) { q = *reinterpret_cast<const uint4*>(p); }
+  __device__ void zero() { q = make_uint4(0, 0, 0, 0); }
+  __device__ void store(uint16_t* p) const { *reinterpret_cast<uint4*>(p) = q; }
+  __device__ void unpack(float (&v)[8]) const {
+    v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x);
+    v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
+    v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z);
+    v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
+  }
+};
+template <>
+struct Chunk8<float> {  // 8 fp32
+  float4 a, b;
+  __device__ void load(const float* p) {
+    a = reinterpret_cast<const float4*>(p)[0];
+    b = reinterpret_cast<const float4*>(p)[1];
+  }
+  __device__ void zero() { a = make_float4(0.f, 0.f, 0.f, 0.f); b = a; }
+  __device__ void store(float* p) const {
+    reinterpret_cast<float4*>(p)[0] = a;
+    reinterpret_cast<float4*>(p)[1] = b;
+  }
+  __device__ void unpack(float (&v)[8]) const {
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
     v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
   }
@@ -88,16 +125,20 @@ __global__ __launch_bounds__(256) void k_router_logits(const ACT* __restrict__ x
     const int64_t b = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
     for (int64_t i = b * 256 + threadIdx.x; i < n_zero; i += nb * 256) zero_words[i] = 0ull;
   }
-  constexpr int XS_BYTES = TT * 512 * (int)sizeof(ACT);
+  constexpr int XS_ELEMS = TT * 512;               // one step of x, TT tokens
+  constexpr int XS_BYTES = 2 * XS_ELEMS * (int)sizeof(ACT);
   constexpr int RED_BYTES = 4 * 32 * 64 * 4;
   constexpr int SMEM = XS_BYTES > RED_BYTES ? XS_BYTES : RED_BYTES;
+  constexpr int XCH = TT * 64;                     // 8-element chunks of a step
+  constexpr int XPT = (XCH + 255) / 256;
   __shared__ __align__(16) unsigned char smem[SMEM];
-  ACT* xs = reinterpret_cast<ACT*>(smem);
+  ACT* xs = reinterpret_cast<ACT*>(smem);          // [2][TT][512]
   float* red = reinterpret_cast<float*>(smem);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t t0 = (int64_t)blockIdx.x * TT;
   const int ew0 = blockIdx.y * 4 * EW + wave * EW;
+  const int NI = (D + 511) / 512;
 
   float acc[TT][EW];
 #pragma unroll
@@ -105,37 +146,46 @@ __global__ __launch_bounds__(256) void k_router_logits(const ACT* __restrict__ x
 #pragma unroll
     for (int e = 0; e < EW; ++e) acc[t][e] = 0.0f;
 
-  for (int i0 = 0; i0 < D; i0 += 512) {
-    __syncthreads();
-    for (int c = threadIdx.x; c < TT * 64; c += 256) {
+  // Ring of depth two: the x chunks (to LDS) and w chunks (registers) of step
+  // i + 1 are loaded before step i is summed.  Out-of-range tokens, experts
+  // and the tail of D are read at clamped addresses and their x chunks
+  // stored as zero (never summed into a stored logit, or zero terms skipped).
+  Chunk8<ACT> xq[XPT], wq[2][EW];
+  auto load = [&](int slot, int i) {
+#pragma unroll
+    for (int u = 0; u < XPT; ++u) {
+      const int c = min((int)threadIdx.x + u * 256, XCH - 1);
       const int tt = c >> 6, j = c & 63;
-      const int d = i0 + 8 * j;
-      ACT* dst = xs + tt * 512 + 8 * j;
-      if (t0 + tt < T && d < D) {
-        const ACT* src = x + (t0 + tt) * (int64_t)D + d;
-        if (sizeof(ACT) == 2) {
-          *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
-        } else {
-          reinterpret_cast<uint4*>(dst)[0] = reinterpret_cast<const uint4*>(src)[0];
-          reinterpret_cast<uint4*>(dst)[1] = reinterpret_cast<const uint4*>(src)[1];
-        }
-      } else {
-        if (sizeof(ACT) == 2) {
-          *reinterpret_cast<uint4*>(dst) = make_uint4(0, 0, 0, 0);
-        } else {
-          reinterpret_cast<uint4*>(dst)[0] = make_uint4(0, 0, 0, 0);
-          reinterpret_cast<uint4*>(dst)[1] = make_uint4(0, 0, 0, 0);
-        }
+      const int64_t t = min(t0 + tt, T - 1);
+      const int d = min(i * 512 + 8 * j, D - 8);
+      xq[u].load(x + t * (int64_t)D + d);
+    }
+    const int d = min(i * 512 + 8 * lane, D - 8);
+#pragma unroll
+    for (int e = 0; e < EW; ++e) wq[slot][e].load(w + (int64_t)min(ew0 + e, E - 1) * D + d);
+  };
+  auto stash = [&](int buf, int i) {
+#pragma unroll
+    for (int u = 0; u < XPT; ++u) {
+      const int c = (int)threadIdx.x + u * 256;
+      if (c < XCH) {
+        const int tt = c >> 6, j = c & 63;
+        Chunk8<ACT> v = xq[u];
+        if (!(t0 + tt < T && i * 512 + 8 * j < D)) v.zero();
+        v.store(xs + buf * XS_ELEMS + tt * 512 + 8 * j);
       }
     }
-    __syncthreads();
-    const int d = i0 + 8 * lane;
+  };
+  auto step = [&](auto slot_c, int i) {
+    constexpr int cur = decltype(slot_c)::value;
+    if (i + 1 < NI) load(cur ^ 1, i + 1);  // uniform
+    const int d = i * 512 + 8 * lane;
     if (d < D) {
       float wv[EW][8];
 #pragma unroll
       for (int e = 0; e < EW; ++e) {
         if (ew0 + e < E) {
-          ActIO<ACT>::load8(w + (int64_t)(ew0 + e) * D + d, wv[e]);
+          wq[cur][e].unpack(wv[e]);
         } else {
 #pragma unroll
           for (int c = 0; c < 8; ++c) wv[e][c] = 0.0f;
@@ -144,45 +194,26 @@ __global__ __launch_bounds__(256) void k_router_logits(const ACT* __restrict__ x
 #pragma unroll
       for (int t = 0; t < TT; ++t) {
         float xv[8];
-        ActIO<ACT>::load8(xs + t * 512 + 8 * lane, xv);
+        ActIO<ACT>::load8(xs + cur * XS_ELEMS + t * 512 + 8 * lane, xv);
 #pragma unroll
         for (int e = 0; e < EW; ++e)
 #pragma unroll
           for (int c = 0; c < 8; ++c) acc[t][e] = __builtin_fmaf(xv[c], wv[e][c], acc[t][e]);
       }
     }
+    if (i + 1 < NI) stash(cur ^ 1, i + 1);
+    __syncthreads();
+  };
+  load(0, 0);
+  stash(0, 0);
+  __syncthreads();
+  for (int i = 0; i < NI; i += 2) {  // ring slots fixed at compile time
+    step(std::integral_constant<int, 0>{}, i);
+    if (i + 1 < NI) step(std::integral_constant<int, 1>{}, i + 1);
   }
 
   logits_tree_store<TT, EW>(acc, red + wave * 32 * 64, t0, ew0, T, E, logits);
 }
-
-// x and w chunks of one 512-wide step, loaded straight into registers
-// (small T): lane j reads elements 8j .. 8j+7 of the step.
-template <typename ACT>
-struct Chunk8;
-template <>
-struct Chunk8<uint16_t> {  // 8 bf16
-  uint4 q;
-  __device__ void load(const uint16_t* p) { q = *reinterpret_cast<const uint4*>(p); }
-  __device__ void unpack(float (&v)[8]) const {
-    v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x);
-    v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
-    v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z);
-    v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
-  }
-};
-template <>
-struct Chunk8<float> {  // 8 fp32
-  float4 a, b;
-  __device__ void load(const float* p) {
-    a = reinterpret_cast<const float4*>(p)[0];
-    b = reinterpret_cast<const float4*>(p)[1];
-  }
-  __device__ void unpack(float (&v)[8]) const {
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  }
-};
 
 // Router logits for small T: the same pairs, partials and order as above, but
 // every lane reads its x and w chunks from global memory into a register ring
@@ -369,8 +400,8 @@ hipError_t launch_router_logits(const void* x, int act, const void* w, int64_t T
   // and how x reaches the lanes; every pair's logit is the same fixed chain.
   // Small T (decode): register ring, latency bound.  Larger T: x staged
   // through LDS once per workgroup (measured faster from a few hundred tokens).
-  if (((T + 15) / 16) * ((E + 31) / 32) >= 512)
-    launch_logits_cfg<16, 8>(x, act, w, T, D, E, logits, zw, nz, s);
+  if (((T + 15) / 16) * ((E + 15) / 16) >= 1024)
+    launch_logits_cfg<16, 4>(x, act, w, T, D, E, logits, zw, nz, s);
   else if (T > 128)
     launch_logits_cfg<4, 2>(x, act, w, T, D, E, logits, zw, nz, s);
   else if (T >= 8)
