@@ -658,6 +658,9 @@ enum TileCfg {
   TILE_WD_128x256,
   TILE_WD_64x128,
   TILE_WD_128x128_P2,
+  TILE_128x128_2x4_P3,  // 8 waves, two per SIMD
+  TILE_128x128_4x2_P3,
+  TILE_128x128_2x4_P2,
   TILE_COUNT,
   TILE_F32 = 100        // fp32 VALU kernel, 16 x 16 tiles
 };
@@ -704,6 +707,9 @@ static TileShape tile_shape(int cfg) {
     case TILE_WD_128x256: return {128, 256};
     case TILE_WD_64x128: return {64, 128};
     case TILE_WD_128x128_P2: return {128, 128};
+    case TILE_128x128_2x4_P3: return {128, 128};
+    case TILE_128x128_4x2_P3: return {128, 128};
+    case TILE_128x128_2x4_P2: return {128, 128};
     default: return {16, 16};  // TILE_F32
   }
 }
@@ -761,6 +767,9 @@ static hipError_t launch_tile_cfg(int cfg, const GemmArgs& a, bool gated, int64_
       if (FP4) return hipErrorInvalidValue;
       return gated ? launch_wd<128, 128, 2, 2, true>(a, grid, st, ev)
                    : launch_wd<128, 128, 2, 2, false>(a, grid, st, ev);
+    case TILE_128x128_2x4_P3: return launch_one<128, 128, 2, 4, 3, FP4>(a, gated, grid, st, ev);
+    case TILE_128x128_4x2_P3: return launch_one<128, 128, 4, 2, 3, FP4>(a, gated, grid, st, ev);
+    case TILE_128x128_2x4_P2: return launch_one<128, 128, 2, 4, 2, FP4>(a, gated, grid, st, ev);
     default: return hipErrorInvalidValue;
   }
 }
@@ -774,7 +783,8 @@ static int pick_tile_cfg(bool gated, int64_t rows_per_group_hint, bool fp4) {
   // (each decoded weight serves more token rows)
   if (fp4 && rows_per_group_hint <= 96) return gated ? TILE_128x64_2x2 : TILE_128x128_2x2_P2;
   if (rows_per_group_hint <= 96) return gated ? TILE_64x32_4x1_P2 : TILE_64x64_4x1_P2;
-  return TILE_128x128_2x2_P2;  // many rows per expert: the largest tile that fits
+  // many rows per expert: 128 x 128 tiles (gate/up on 8 waves, two per SIMD)
+  return gated ? TILE_128x128_2x4_P2 : TILE_128x128_2x2_P2;
 }
 
 GemmPlan plan_grouped_gemm(const SegShape* segs, int nseg, bool gated, int act,
