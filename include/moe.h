@@ -74,7 +74,7 @@ typedef enum {
   MOE_ERR_DTYPE = -3,       /* unsupported dtype combination */
   MOE_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
   MOE_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than required */
-  MOE_ERR_UNSUPPORTED = -6, /* valid request this build does not implement */
+  MOE_ERR_UNSUPPORTED = -6, /* valid request that the library does not implement */
   MOE_ERR_HIP = -7          /* a HIP launch failed */
 } moe_status;
 
