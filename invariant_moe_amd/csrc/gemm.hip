@@ -355,190 +355,6 @@ __global__ __launch_bounds__(64 * WM * WN) void k_grouped_gemm_bf16(GemmArgs arg
 }
 
 // ---------------------------------------------------------------------------
-// Weights-direct MFMA kernel for compute-bound tiles (bf16 weights).  Four
-// waves; wave w owns features [n0 + w*BN/4, n0 + (w+1)*BN/4) of each matrix
-// and all BM token rows.  Each wave loads its weight fragments straight from
-// global memory into registers in the MFMA operand layout (lane: row
-// lane % 16 of a 16-feature block, 8 consecutive k at 8 * (lane / 16)), PW
-// stages ahead; only the token tile, which the four waves share, goes through
-// LDS (PX stages in flight, two LDS buffers).  Half the LDS traffic of the
-// kernel above and a deeper weight prefetch, for the same instruction,
-// operands and K order, so the same bits: full 64-wide stages, then the one
-// trailing 32-wide step (the last 32 of K, or zeros).
-// ---------------------------------------------------------------------------
-template <int BM, int BN, int PW, int PX, bool GATED>
-__global__ __launch_bounds__(256) void k_grouped_gemm_wd(GemmArgs args) {
-  constexpr int NT = 256;
-  constexpr int NMAT = GATED ? 2 : 1;
-  constexpr int TBW = BM / 16;
-  constexpr int NBW = BN / 64;  // 16-feature blocks per wave per matrix
-  static_assert(NBW >= 1 && TBW >= 1 && PW % PX == 0, "tile / pipeline shape");
-  constexpr int XCH = BM * (KT / 8);
-  constexpr int XPT = (XCH + NT - 1) / NT;
-  __shared__ __align__(16) uint16_t xs[2][BM * LDK];
-
-  TileInfo ti;
-  if (!read_tile(args, BM, ti)) return;
-  const GemmSeg& s = args.seg[ti.seg];
-  const int K = s.K, N = s.N;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-  // token rows of this thread's chunks (clamped into the tile); indices first
-  int64_t xrow[XPT];
-#pragma unroll
-  for (int i = 0; i < XPT; ++i) {
-    const int c = tid + i * NT;
-    xrow[i] = ti.row0 + min(min(c / (KT / 8), BM - 1), ti.rows - 1);
-  }
-  if (s.a_index) {
-#pragma unroll
-    for (int i = 0; i < XPT; ++i) xrow[i] = s.a_index[xrow[i]];
-  }
-  const uint16_t* wsrc[NMAT][NBW];
-#pragma unroll
-  for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) {
-      const int n = min(ti.n0 + wave * (BN / 4) + nb * 16 + (lane & 15), N - 1);
-      const uint16_t* base = static_cast<const uint16_t*>(m ? s.W1 : s.W0);
-      wsrc[m][nb] = base + ((int64_t)ti.g * N + n) * K + 8 * (lane >> 4);
-    }
-
-  f32x4_t acc[NMAT][NBW][TBW];
-#pragma unroll
-  for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-    for (int nb = 0; nb < NBW; ++nb)
-#pragma unroll
-      for (int tb = 0; tb < TBW; ++tb) acc[m][nb][tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  uint4 wf[PW][NMAT][NBW][2];  // weight fragments of PW stages (k-steps 0, 1)
-  uint4 xr[PX][XPT];
-  const uint16_t* xsrc[XPT];
-  const int nkf = K / KT;
-
-  auto wload = [&](uint4 (&w)[NMAT][NBW][2], int kt) {
-    const int k0 = kt * KT;
-#pragma unroll
-    for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-      for (int nb = 0; nb < NBW; ++nb)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          w[m][nb][ks] = *reinterpret_cast<const uint4*>(wsrc[m][nb] + k0 + ks * 32);
-  };
-  auto xload = [&](uint4 (&xq)[XPT], int kt, bool half) {
-    const int k0 = kt * KT;
-    const bool none = half && (K % KT) == 0;
-#pragma unroll
-    for (int i = 0; i < XPT; ++i) {
-      const int c = tid + i * NT;
-      if (half && (none || (c % (KT / 8)) >= 4))
-        xq[i] = make_uint4(0, 0, 0, 0);
-      else
-        xq[i] = *reinterpret_cast<const uint4*>(xsrc[i] + k0);
-    }
-  };
-  auto xstore = [&](const uint4 (&xq)[XPT], int buf) {
-#pragma unroll
-    for (int i = 0; i < XPT; ++i) {
-      const int c = tid + i * NT;
-      if (c < XCH) *reinterpret_cast<uint4*>(&xs[buf][(c / (KT / 8)) * LDK + (c % (KT / 8)) * 8]) = xq[i];
-    }
-  };
-  auto compute = [&](const uint4 (&w)[NMAT][NBW][2], int buf, auto ksteps_c) {
-    constexpr int KSTEPS = decltype(ksteps_c)::value;
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      bf16x8_t bfr[TBW];
-#pragma unroll
-      for (int tb = 0; tb < TBW; ++tb) {
-        const int r = tb * 16 + (lane & 15);
-        bfr[tb] = *reinterpret_cast<const bf16x8_t*>(&xs[buf][r * LDK + ks * 32 + 8 * (lane >> 4)]);
-      }
-#pragma unroll
-      for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-        for (int nb = 0; nb < NBW; ++nb) {
-          const bf16x8_t a = __builtin_bit_cast(bf16x8_t, w[m][nb][ks]);
-#pragma unroll
-          for (int tb = 0; tb < TBW; ++tb)
-            acc[m][nb][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bfr[tb], acc[m][nb][tb], 0, 0, 0);
-        }
-    }
-  };
-
-  using two = std::integral_constant<int, 2>;
-  using one = std::integral_constant<int, 1>;
-  if (nkf > 0) {
-#pragma unroll
-    for (int q = 0; q < PW; ++q) wload(wf[q], min(q, nkf - 1));
-  }
-  // the weight stream does not depend on the token rows
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int i = 0; i < XPT; ++i) {
-    const int c = tid + i * NT;
-    xsrc[i] = static_cast<const uint16_t*>(s.A) + xrow[i] * K + (c % (KT / 8)) * 8;
-  }
-  if (nkf > 0) {
-#pragma unroll
-    for (int q = 0; q < PX; ++q) xload(xr[q], min(q, nkf - 1), false);
-    xstore(xr[0], 0);
-    __syncthreads();
-    // Iteration kt computes stage kt (weights in slot kt % PW, tokens in LDS
-    // buffer kt & 1), refills that weight slot with stage kt + PW and token
-    // slot kt % PX (already in LDS) with stage kt + PX, then moves the tokens
-    // of stage kt + 1 (slot (kt + 1) % PX) into the other LDS buffer.  Loads
-    // past the last stage read it again (clamped) and are never used.
-    const int niter = (nkf + PW - 1) / PW * PW;
-    for (int kt0 = 0; kt0 < niter; kt0 += PW) {
-#pragma unroll
-      for (int q = 0; q < PW; ++q) {
-        const int kt = kt0 + q;
-        if (kt < nkf) compute(wf[q], kt & 1, two{});
-        wload(wf[q], min(kt + PW, nkf - 1));
-        xload(xr[q % PX], min(kt + PX, nkf - 1), false);
-        xstore(xr[(q + 1) % PX], (kt + 1) & 1);
-        __syncthreads();
-      }
-    }
-  }
-  // Trailing k-step: the last 32 of K when K % 64 == 32, zeros otherwise.
-  uint4 wt[NMAT][NBW][2];
-#pragma unroll
-  for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) {
-      wt[m][nb][1] = make_uint4(0, 0, 0, 0);
-      wt[m][nb][0] = (K % KT) == 32
-                         ? *reinterpret_cast<const uint4*>(wsrc[m][nb] + nkf * KT)
-                         : make_uint4(0, 0, 0, 0);
-    }
-  xload(xr[0], nkf, true);
-  xstore(xr[0], nkf & 1);
-  __syncthreads();
-  compute(wt, nkf & 1, one{});
-
-  uint16_t* out = static_cast<uint16_t*>(s.out);
-#pragma unroll
-  for (int nb = 0; nb < NBW; ++nb)
-#pragma unroll
-    for (int tb = 0; tb < TBW; ++tb) {
-      const int r = tb * 16 + (lane & 15);
-      const int n = ti.n0 + wave * (BN / 4) + nb * 16 + 4 * (lane >> 4);
-      if (r < ti.rows && n < N) {
-        float v[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          v[i] = GATED ? silu_mul(acc[0][nb][tb][i], acc[NMAT - 1][nb][tb][i]) : acc[0][nb][tb][i];
-        uint2 pk = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-        *reinterpret_cast<uint2*>(out + (ti.row0 + r) * (int64_t)N + n) = pk;
-      }
-    }
-}
-
-// ---------------------------------------------------------------------------
 // fp32 kernel (VALU): each output element is one fmaf chain over K in
 // increasing order from +0, whatever the tile.  Tile 16 rows x 16 features.
 // ---------------------------------------------------------------------------
@@ -611,58 +427,20 @@ static hipError_t launch_one(const GemmArgs& a, bool gated, int64_t grid, hipStr
   return hipGetLastError();
 }
 
-template <int BM, int BN, int PW, int PX, bool GATED>
-static hipError_t launch_wd(const GemmArgs& a, int64_t grid, hipStream_t st, LaunchEvents ev) {
-  hipExtLaunchKernelGGL((k_grouped_gemm_wd<BM, BN, PW, PX, GATED>), dim3((unsigned)grid),
-                        dim3(256), 0, st, ev.start, ev.stop, 0, a);
-  return hipGetLastError();
-}
-
 // Tile configurations (BM token rows, BN features, WM x WN waves, P stages in
 // flight).  Every configuration computes identical bits (same MFMA chain per
 // output element); they differ in occupancy, workgroup count and reuse.
 enum TileCfg {
-  TILE_16x16_1x1 = 0,   // one wave: decode, many small workgroups
-  TILE_16x32_1x2,
-  TILE_16x64_1x4,
-  TILE_32x64_1x4,
-  TILE_64x64_1x4,
-  TILE_64x64_4x1,
-  TILE_64x64_2x2,
-  TILE_128x64_4x1,
-  TILE_128x64_2x2,
-  TILE_64x32_4x1,
-  TILE_128x32_4x1,
-  TILE_32x32_2x1,
-  TILE_64x32_2x2,
+  TILE_16x32_1x2_P4 = 0,  // decode: few rows per expert, many small workgroups
+  TILE_16x64_1x4_P4,
+  TILE_32x64_1x4_P4,
+  TILE_64x32_4x1_P2,      // tens of rows per expert
   TILE_64x64_4x1_P2,
-  TILE_32x64_2x2,
-  TILE_64x128_2x2,
-  TILE_64x128_1x4,
-  TILE_64x16_4x1,
-  TILE_128x16_4x1,
-  TILE_64x32_4x1_P2,
-  TILE_32x64_2x2_P2,
-  TILE_64x64_2x2_P2,
-  TILE_64x128_2x2_P2,
-  TILE_64x64_4x1_P3,
-  TILE_128x64_4x1_P2,
-  TILE_16x32_1x2_P8,
-  TILE_16x64_1x4_P8,
-  TILE_16x32_1x2_P6,
-  TILE_16x64_1x4_P6,
-  TILE_16x16_1x1_P8,
-  TILE_256x128_4x2_P2,  // 8 waves, 64x64 (x2 matrices) per wave: compute-bound shapes
-  TILE_128x128_2x2_P2,
-  TILE_WD_128x128,      // weights-direct (bf16 weights only; MXFP4 falls back)
-  TILE_WD_128x256,
-  TILE_WD_64x128,
-  TILE_WD_128x128_P2,
-  TILE_128x128_2x4_P3,  // 8 waves, two per SIMD
-  TILE_128x128_4x2_P3,
-  TILE_128x128_2x4_P2,
+  TILE_128x64_2x2_P3,     // MXFP4 weights with tens of rows per expert
+  TILE_128x128_2x2_P2,    // prefill
+  TILE_128x128_2x4_P2,    // prefill gate/up: 8 waves, two per SIMD
   TILE_COUNT,
-  TILE_F32 = 100        // fp32 VALU kernel, 16 x 16 tiles
+  TILE_F32 = 100          // fp32 VALU kernel, 16 x 16 tiles
 };
 
 struct TileShape {
@@ -671,44 +449,13 @@ struct TileShape {
 
 static TileShape tile_shape(int cfg) {
   switch (cfg) {
-    case TILE_16x16_1x1: return {16, 16};
-    case TILE_16x32_1x2: return {16, 32};
-    case TILE_16x64_1x4: return {16, 64};
-    case TILE_32x64_1x4: return {32, 64};
-    case TILE_64x64_1x4: return {64, 64};
-    case TILE_64x64_4x1: return {64, 64};
-    case TILE_64x64_2x2: return {64, 64};
-    case TILE_128x64_4x1: return {128, 64};
-    case TILE_128x64_2x2: return {128, 64};
-    case TILE_64x32_4x1: return {64, 32};
-    case TILE_128x32_4x1: return {128, 32};
-    case TILE_32x32_2x1: return {32, 32};
-    case TILE_64x32_2x2: return {64, 32};
-    case TILE_64x64_4x1_P2: return {64, 64};
-    case TILE_32x64_2x2: return {32, 64};
-    case TILE_64x128_2x2: return {64, 128};
-    case TILE_64x128_1x4: return {64, 128};
-    case TILE_64x16_4x1: return {64, 16};
-    case TILE_128x16_4x1: return {128, 16};
+    case TILE_16x32_1x2_P4: return {16, 32};
+    case TILE_16x64_1x4_P4: return {16, 64};
+    case TILE_32x64_1x4_P4: return {32, 64};
     case TILE_64x32_4x1_P2: return {64, 32};
-    case TILE_32x64_2x2_P2: return {32, 64};
-    case TILE_64x64_2x2_P2: return {64, 64};
-    case TILE_64x128_2x2_P2: return {64, 128};
-    case TILE_64x64_4x1_P3: return {64, 64};
-    case TILE_128x64_4x1_P2: return {128, 64};
-    case TILE_16x32_1x2_P8: return {16, 32};
-    case TILE_16x64_1x4_P8: return {16, 64};
-    case TILE_16x32_1x2_P6: return {16, 32};
-    case TILE_16x64_1x4_P6: return {16, 64};
-    case TILE_16x16_1x1_P8: return {16, 16};
-    case TILE_256x128_4x2_P2: return {256, 128};
+    case TILE_64x64_4x1_P2: return {64, 64};
+    case TILE_128x64_2x2_P3: return {128, 64};
     case TILE_128x128_2x2_P2: return {128, 128};
-    case TILE_WD_128x128: return {128, 128};
-    case TILE_WD_128x256: return {128, 256};
-    case TILE_WD_64x128: return {64, 128};
-    case TILE_WD_128x128_P2: return {128, 128};
-    case TILE_128x128_2x4_P3: return {128, 128};
-    case TILE_128x128_4x2_P3: return {128, 128};
     case TILE_128x128_2x4_P2: return {128, 128};
     default: return {16, 16};  // TILE_F32
   }
@@ -718,57 +465,13 @@ template <bool FP4>
 static hipError_t launch_tile_cfg(int cfg, const GemmArgs& a, bool gated, int64_t grid,
                                   hipStream_t st, LaunchEvents ev) {
   switch (cfg) {
-    case TILE_16x16_1x1: return launch_one<16, 16, 1, 1, 4, FP4>(a, gated, grid, st, ev);
-    case TILE_16x32_1x2: return launch_one<16, 32, 1, 2, 4, FP4>(a, gated, grid, st, ev);
-    case TILE_16x64_1x4: return launch_one<16, 64, 1, 4, 4, FP4>(a, gated, grid, st, ev);
-    case TILE_32x64_1x4: return launch_one<32, 64, 1, 4, 4, FP4>(a, gated, grid, st, ev);
-    case TILE_64x64_1x4: return launch_one<64, 64, 1, 4, 4, FP4>(a, gated, grid, st, ev);
-    case TILE_64x64_4x1: return launch_one<64, 64, 4, 1, 4, FP4>(a, gated, grid, st, ev);
-    case TILE_64x64_2x2: return launch_one<64, 64, 2, 2, 4, FP4>(a, gated, grid, st, ev);
-    case TILE_128x64_4x1: return launch_one<128, 64, 4, 1, 3, FP4>(a, gated, grid, st, ev);
-    case TILE_128x64_2x2: return launch_one<128, 64, 2, 2, 3, FP4>(a, gated, grid, st, ev);
-    case TILE_64x32_4x1: return launch_one<64, 32, 4, 1, 4, FP4>(a, gated, grid, st, ev);
-    case TILE_128x32_4x1: return launch_one<128, 32, 4, 1, 4, FP4>(a, gated, grid, st, ev);
-    case TILE_32x32_2x1: return launch_one<32, 32, 2, 1, 4, FP4>(a, gated, grid, st, ev);
-    case TILE_64x32_2x2: return launch_one<64, 32, 2, 2, 4, FP4>(a, gated, grid, st, ev);
-    case TILE_64x64_4x1_P2: return launch_one<64, 64, 4, 1, 2, FP4>(a, gated, grid, st, ev);
-    case TILE_32x64_2x2: return launch_one<32, 64, 2, 2, 4, FP4>(a, gated, grid, st, ev);
-    case TILE_64x128_2x2: return launch_one<64, 128, 2, 2, 4, FP4>(a, gated, grid, st, ev);
-    case TILE_64x128_1x4: return launch_one<64, 128, 1, 4, 4, FP4>(a, gated, grid, st, ev);
-    case TILE_64x16_4x1: return launch_one<64, 16, 4, 1, 4, FP4>(a, gated, grid, st, ev);
-    case TILE_128x16_4x1: return launch_one<128, 16, 4, 1, 4, FP4>(a, gated, grid, st, ev);
+    case TILE_16x32_1x2_P4: return launch_one<16, 32, 1, 2, 4, FP4>(a, gated, grid, st, ev);
+    case TILE_16x64_1x4_P4: return launch_one<16, 64, 1, 4, 4, FP4>(a, gated, grid, st, ev);
+    case TILE_32x64_1x4_P4: return launch_one<32, 64, 1, 4, 4, FP4>(a, gated, grid, st, ev);
     case TILE_64x32_4x1_P2: return launch_one<64, 32, 4, 1, 2, FP4>(a, gated, grid, st, ev);
-    case TILE_32x64_2x2_P2: return launch_one<32, 64, 2, 2, 2, FP4>(a, gated, grid, st, ev);
-    case TILE_64x64_2x2_P2: return launch_one<64, 64, 2, 2, 2, FP4>(a, gated, grid, st, ev);
-    case TILE_64x128_2x2_P2: return launch_one<64, 128, 2, 2, 2, FP4>(a, gated, grid, st, ev);
-    case TILE_64x64_4x1_P3: return launch_one<64, 64, 4, 1, 3, FP4>(a, gated, grid, st, ev);
-    case TILE_128x64_4x1_P2: return launch_one<128, 64, 4, 1, 2, FP4>(a, gated, grid, st, ev);
-    case TILE_16x32_1x2_P8: return launch_one<16, 32, 1, 2, 8, FP4>(a, gated, grid, st, ev);
-    case TILE_16x64_1x4_P8: return launch_one<16, 64, 1, 4, 8, FP4>(a, gated, grid, st, ev);
-    case TILE_16x32_1x2_P6: return launch_one<16, 32, 1, 2, 6, FP4>(a, gated, grid, st, ev);
-    case TILE_16x64_1x4_P6: return launch_one<16, 64, 1, 4, 6, FP4>(a, gated, grid, st, ev);
-    case TILE_16x16_1x1_P8: return launch_one<16, 16, 1, 1, 8, FP4>(a, gated, grid, st, ev);
-    case TILE_256x128_4x2_P2: return launch_one<256, 128, 4, 2, 2, FP4>(a, gated, grid, st, ev);
+    case TILE_64x64_4x1_P2: return launch_one<64, 64, 4, 1, 2, FP4>(a, gated, grid, st, ev);
+    case TILE_128x64_2x2_P3: return launch_one<128, 64, 2, 2, 3, FP4>(a, gated, grid, st, ev);
     case TILE_128x128_2x2_P2: return launch_one<128, 128, 2, 2, 2, FP4>(a, gated, grid, st, ev);
-    // weights-direct: bf16 weights only (the planner never picks these for
-    // MXFP4); 128x256 exists for the down projection only.
-    case TILE_WD_128x128:
-      if (FP4) return hipErrorInvalidValue;
-      return gated ? launch_wd<128, 128, 4, 2, true>(a, grid, st, ev)
-                   : launch_wd<128, 128, 4, 2, false>(a, grid, st, ev);
-    case TILE_WD_128x256:
-      if (FP4 || gated) return hipErrorInvalidValue;
-      return launch_wd<128, 256, 4, 2, false>(a, grid, st, ev);
-    case TILE_WD_64x128:
-      if (FP4) return hipErrorInvalidValue;
-      return gated ? launch_wd<64, 128, 4, 2, true>(a, grid, st, ev)
-                   : launch_wd<64, 128, 4, 2, false>(a, grid, st, ev);
-    case TILE_WD_128x128_P2:
-      if (FP4) return hipErrorInvalidValue;
-      return gated ? launch_wd<128, 128, 2, 2, true>(a, grid, st, ev)
-                   : launch_wd<128, 128, 2, 2, false>(a, grid, st, ev);
-    case TILE_128x128_2x4_P3: return launch_one<128, 128, 2, 4, 3, FP4>(a, gated, grid, st, ev);
-    case TILE_128x128_4x2_P3: return launch_one<128, 128, 4, 2, 3, FP4>(a, gated, grid, st, ev);
     case TILE_128x128_2x4_P2: return launch_one<128, 128, 2, 4, 2, FP4>(a, gated, grid, st, ev);
     default: return hipErrorInvalidValue;
   }
@@ -777,11 +480,11 @@ static hipError_t launch_tile_cfg(int cfg, const GemmArgs& a, bool gated, int64_
 // Host-side choice from the average rows per group (no device sync), from
 // measured sweeps on MI355X (all choices give identical bits).
 static int pick_tile_cfg(bool gated, int64_t rows_per_group_hint, bool fp4) {
-  if (rows_per_group_hint <= 2) return gated ? TILE_16x32_1x2 : TILE_16x64_1x4;
-  if (rows_per_group_hint <= 16) return TILE_32x64_1x4;
+  if (rows_per_group_hint <= 2) return gated ? TILE_16x32_1x2_P4 : TILE_16x64_1x4_P4;
+  if (rows_per_group_hint <= 16) return TILE_32x64_1x4_P4;
   // MXFP4 weights: the decode in the LDS staging favours 128-row tiles
   // (each decoded weight serves more token rows)
-  if (fp4 && rows_per_group_hint <= 96) return gated ? TILE_128x64_2x2 : TILE_128x128_2x2_P2;
+  if (fp4 && rows_per_group_hint <= 96) return gated ? TILE_128x64_2x2_P3 : TILE_128x128_2x2_P2;
   if (rows_per_group_hint <= 96) return gated ? TILE_64x32_4x1_P2 : TILE_64x64_4x1_P2;
   // many rows per expert: 128 x 128 tiles (gate/up on 8 waves, two per SIMD)
   return gated ? TILE_128x128_2x4_P2 : TILE_128x128_2x2_P2;
@@ -797,7 +500,6 @@ GemmPlan plan_grouped_gemm(const SegShape* segs, int nseg, bool gated, int act,
   for (int i = 0; i < nseg; ++i) p.seg[i] = segs[i];
   const int cfg = act == MOE_F32 ? (int)TILE_F32
                                   : pick_tile_cfg(gated, rows_per_group_hint, segs[0].wfmt != 0);
-  const TileShape ts = tile_shape(cfg);
   // Segments with the same weight format share one launch; a mixed pair
   // (MXFP4 routed experts + bf16 shared expert) takes one launch per format.
   const bool split = nseg == 2 && segs[0].wfmt != segs[1].wfmt;
@@ -805,13 +507,7 @@ GemmPlan plan_grouped_gemm(const SegShape* segs, int nseg, bool gated, int act,
   for (int l = 0; l < nl; ++l) {
     PlanLaunch& L = p.l[p.n];
     L.seg_mask = split ? (1 << l) : (nseg == 2 ? 3 : 1);
-    const int first = (L.seg_mask & 1) ? 0 : 1;
-    // weights-direct tiles read bf16 weights; an MXFP4 launch takes the LDS
-    // kernel with the same row tile (the tables of all launches share BM)
-    const bool wd = cfg == TILE_WD_128x128 || cfg == TILE_WD_128x256 ||
-                    cfg == TILE_WD_64x128 || cfg == TILE_WD_128x128_P2;
-    L.cfg = (wd && segs[first].wfmt) ? (ts.BM == 64 ? (int)TILE_64x64_2x2 : (int)TILE_128x64_2x2)
-                                     : cfg;
+    L.cfg = cfg;
     const TileShape ls = tile_shape(L.cfg);
     L.BM = ls.BM;
     L.BN = ls.BN;
