@@ -30,6 +30,15 @@
 
 namespace moe {
 
+// Calls f(integral_constant<int, I>) for I = B..E-1.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 constexpr int KT = 64;         // K per LDS stage (two MFMA k-steps)
 constexpr int LDK = KT + 8;    // padded LDS row (bf16 elements) -> 144 B stride
 
@@ -90,7 +99,7 @@ __device__ __forceinline__ void decode_mxfp4_32(const uint4 q, uint32_t sbyte, u
 // WM x WN grid; each wave holds TBW token blocks x NBW feature blocks of 16.
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int WM, int WN, int P, bool GATED, bool FP4>
-__global__ __launch_bounds__(64 * WM * WN) void k_grouped_gemm_bf16(GemmArgs args) {
+__global__ __launch_bounds__(64 * WM * WN, 2) void k_grouped_gemm_bf16(GemmArgs args) {
   constexpr int NT = 64 * WM * WN;
   constexpr int NMAT = GATED ? 2 : 1;
   constexpr int TBW = BM / 16 / WM;
@@ -230,21 +239,21 @@ __global__ __launch_bounds__(64 * WM * WN) void k_grouped_gemm_bf16(GemmArgs arg
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
       const int c = tid + i * NT;
-      if (c < XCH)
+      if (XCH % NT == 0 || c < XCH)
         *reinterpret_cast<uint4*>(&Xs[(c / (KT / 8)) * LDK + (c % (KT / 8)) * 8]) = xq[i];
     }
     if constexpr (!fp4) {
 #pragma unroll
       for (int i = 0; i < WPT; ++i) {
         const int c = tid + i * NT;
-        if (c < WCH)
+        if (WCH % NT == 0 || c < WCH)
           *reinterpret_cast<uint4*>(&Ws[(c / (KT / 8)) * LDK + (c % (KT / 8)) * 8]) = wq[i];
       }
     } else {
 #pragma unroll
       for (int i = 0; i < QPT; ++i) {
         const int c = tid + i * NT;
-        if (c < QCH) {
+        if (QCH % NT == 0 || c < QCH) {
           uint32_t o[16];
           decode_mxfp4_32(wq[i], sq[i], o);
           uint4* dst = reinterpret_cast<uint4*>(&Ws[(c / 2) * LDK + (c % 2) * 32]);
@@ -257,46 +266,70 @@ __global__ __launch_bounds__(64 * WM * WN) void k_grouped_gemm_bf16(GemmArgs arg
     }
   };
   // The fixed per-element chain: for each 32-wide k-step in increasing order,
-  // acc = mfma(weights, tokens, acc).
-  auto compute = [&](int buf, auto ksteps_c) {
-    constexpr int KSTEPS = decltype(ksteps_c)::value;
+  // acc = mfma(weights, tokens, acc).  One k-step's operands are read from
+  // LDS into a fragment set, so that the reads of the next k-step are in
+  // flight while the MFMAs of this one run.
+  struct Frag {
+    bf16x8_t a[NMAT][NBW];
+    bf16x8_t b[TBW];
+  };
+  auto read_frag = [&](Frag& f, int buf, int ks) {
     const uint16_t* Xs = lds + buf * BUF;
     const uint16_t* Ws = Xs + BM * LDK;
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      bf16x8_t af[NMAT][NBW], bfr[TBW];
+    for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-      for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-        for (int nb = 0; nb < NBW; ++nb) {
-          const int n = m * BN + (wn * NBW + nb) * 16 + (lane & 15);
-          af[m][nb] = *reinterpret_cast<const bf16x8_t*>(&Ws[n * LDK + ks * 32 + 8 * (lane >> 4)]);
-        }
-#pragma unroll
-      for (int tb = 0; tb < TBW; ++tb) {
-        const int r = (wm * TBW + tb) * 16 + (lane & 15);
-        bfr[tb] = *reinterpret_cast<const bf16x8_t*>(&Xs[r * LDK + ks * 32 + 8 * (lane >> 4)]);
+      for (int nb = 0; nb < NBW; ++nb) {
+        const int n = m * BN + (wn * NBW + nb) * 16 + (lane & 15);
+        f.a[m][nb] = *reinterpret_cast<const bf16x8_t*>(&Ws[n * LDK + ks * 32 + 8 * (lane >> 4)]);
       }
 #pragma unroll
-      for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-        for (int nb = 0; nb < NBW; ++nb)
-#pragma unroll
-          for (int tb = 0; tb < TBW; ++tb)
-            acc[m][nb][tb] =
-                __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[m][nb], bfr[tb], acc[m][nb][tb], 0, 0, 0);
+    for (int tb = 0; tb < TBW; ++tb) {
+      const int r = (wm * TBW + tb) * 16 + (lane & 15);
+      f.b[tb] = *reinterpret_cast<const bf16x8_t*>(&Xs[r * LDK + ks * 32 + 8 * (lane >> 4)]);
     }
   };
+  auto mma = [&](const Frag& f) {
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+        for (int tb = 0; tb < TBW; ++tb)
+          acc[m][nb][tb] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[m][nb], f.b[tb], acc[m][nb][tb], 0, 0, 0);
+  };
 
-  // Full 64-wide stages 0..nkf-1 run through one pipelined loop: stage s
-  // lives in register slot s % P.  Iteration k issues the loads of stage k+P
-  // (clamped to the last stage) into the slot stage k used, computes stage k
-  // from LDS buffer k&1, moves stage k+1 from registers into LDS buffer
-  // (k+1)&1, then one barrier.  The loop runs a multiple of P iterations; the
-  // extra ones skip the compute (uniform branch) and store data nobody reads.
-  using two = std::integral_constant<int, 2>;
-  using one = std::integral_constant<int, 1>;
+  // Full 64-wide stages 0..nkf-1.  Stage s lives in register slot s % P until
+  // it is written to LDS buffer s & 1.  Step k (slot q = k % P):
+  //   issue the loads of stage k+P (clamped to the last stage) into slot q,
+  //   which stage k left at step k-1;
+  //   read the second k-step of stage k (fragment set fb);
+  //   write stage k+1 from its slot into buffer (k+1)&1, whose last readers
+  //   (stage k-1) finished before the previous barrier;
+  //   MFMAs of the first k-step of stage k (fa);
+  //   barrier: stage k+1 is in LDS, buffer k&1 is no longer read;
+  //   read the first k-step of stage k+1 into fa (on the last step this
+  //   reads a buffer nobody uses and fa is overwritten afterwards);
+  //   MFMAs of the second k-step of stage k (fb), covering those reads.
+  // Full groups of P steps run branch-free; the remaining nkf % P steps
+  // follow with uniform guards.
   const int nkf = K / KT;
+  Frag fa, fb;
+  auto step = [&](auto qc, int k) {
+    constexpr int q = decltype(qc)::value;
+    gload(xr[q], wr[q], sr[q], min(k + P, nkf - 1), false);
+    read_frag(fb, k & 1, 1);
+    lstore(xr[(q + 1) % P], wr[(q + 1) % P], sr[(q + 1) % P], (k + 1) & 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(fa);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    read_frag(fa, (k + 1) & 1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(fb);
+    __builtin_amdgcn_sched_barrier(0);
+  };
   if (nkf > 0) {
 #pragma unroll
     for (int q = 0; q < P; ++q) gload_w(wr[q], sr[q], min(q, nkf - 1), false);
@@ -314,25 +347,22 @@ __global__ __launch_bounds__(64 * WM * WN) void k_grouped_gemm_bf16(GemmArgs arg
     for (int q = 0; q < P; ++q) gload_x(xr[q], min(q, nkf - 1), false);
     lstore(xr[0], wr[0], sr[0], 0);
     __syncthreads();
-    const int niter = (nkf + P - 1) / P * P;
-    for (int kt = 0; kt < niter; kt += P) {
-#pragma unroll
-      for (int q = 0; q < P; ++q) {
-        const int k = kt + q;
-        gload(xr[q], wr[q], sr[q], min(k + P, nkf - 1), false);
-        if (k < nkf) compute(k & 1, two{});
-        lstore(xr[(q + 1) % P], wr[(q + 1) % P], sr[(q + 1) % P], (k + 1) & 1);
-        __syncthreads();
-      }
-    }
+    read_frag(fa, 0, 0);
+    const int nfull = nkf / P * P;
+    for (int kt = 0; kt < nfull; kt += P) static_for<0, P>([&](auto qc) { step(qc, kt + qc); });
+    static_for<0, P>([&](auto qc) {
+      if (nfull + qc < nkf) step(qc, nfull + qc);
+    });
   }
   // Trailing k-step: the last 32 of K when K % 64 == 32, and a step over zero
   // operands otherwise.  Running it unconditionally keeps one chain for every
   // tile variant (a zero step leaves every nonzero accumulator unchanged).
+  // Buffer nkf&1 was last read for stage nkf-2, before the last barrier.
   gload(xr[0], wr[0], sr[0], nkf, true);
   lstore(xr[0], wr[0], sr[0], nkf & 1);
   __syncthreads();
-  compute(nkf & 1, one{});
+  read_frag(fa, nkf & 1, 0);
+  mma(fa);
 
   // epilogue: lane holds features n = base + 4*(lane/16) + i (i = 0..3) of
   // token row base + lane%16 -> one 8-byte store of 4 bf16.
@@ -415,15 +445,10 @@ struct LaunchEvents {
   hipEvent_t start, stop;
 };
 
-template <int BM, int BN, int WM, int WN, int P, bool FP4>
-static hipError_t launch_one(const GemmArgs& a, bool gated, int64_t grid, hipStream_t st,
-                             LaunchEvents ev) {
-  if (gated)
-    hipExtLaunchKernelGGL((k_grouped_gemm_bf16<BM, BN, WM, WN, P, true, FP4>),
-                          dim3((unsigned)grid), dim3(64 * WM * WN), 0, st, ev.start, ev.stop, 0, a);
-  else
-    hipExtLaunchKernelGGL((k_grouped_gemm_bf16<BM, BN, WM, WN, P, false, FP4>),
-                          dim3((unsigned)grid), dim3(64 * WM * WN), 0, st, ev.start, ev.stop, 0, a);
+template <int BM, int BN, int WM, int WN, int P, bool GATED, bool FP4>
+static hipError_t launch_one(const GemmArgs& a, int64_t grid, hipStream_t st, LaunchEvents ev) {
+  hipExtLaunchKernelGGL((k_grouped_gemm_bf16<BM, BN, WM, WN, P, GATED, FP4>),
+                        dim3((unsigned)grid), dim3(64 * WM * WN), 0, st, ev.start, ev.stop, 0, a);
   return hipGetLastError();
 }
 
@@ -461,20 +486,35 @@ static TileShape tile_shape(int cfg) {
   }
 }
 
+// The (configuration, branch, weight format) combinations the planner can
+// select: every configuration for either format, since a launch of one
+// format may carry the configuration chosen for the other (shared and routed
+// experts in different formats), except the 128 x 64 gate/up tile, which only
+// MXFP4 launches get (a bf16 launch takes its twin of the same row tile).
 template <bool FP4>
 static hipError_t launch_tile_cfg(int cfg, const GemmArgs& a, bool gated, int64_t grid,
                                   hipStream_t st, LaunchEvents ev) {
-  switch (cfg) {
-    case TILE_16x32_1x2_P4: return launch_one<16, 32, 1, 2, 4, FP4>(a, gated, grid, st, ev);
-    case TILE_16x64_1x4_P4: return launch_one<16, 64, 1, 4, 4, FP4>(a, gated, grid, st, ev);
-    case TILE_32x64_1x4_P4: return launch_one<32, 64, 1, 4, 4, FP4>(a, gated, grid, st, ev);
-    case TILE_64x32_4x1_P2: return launch_one<64, 32, 4, 1, 2, FP4>(a, gated, grid, st, ev);
-    case TILE_64x64_4x1_P2: return launch_one<64, 64, 4, 1, 2, FP4>(a, gated, grid, st, ev);
-    case TILE_128x64_2x2_P3: return launch_one<128, 64, 2, 2, 3, FP4>(a, gated, grid, st, ev);
-    case TILE_128x128_2x2_P2: return launch_one<128, 128, 2, 2, 2, FP4>(a, gated, grid, st, ev);
-    case TILE_128x128_2x4_P2: return launch_one<128, 128, 2, 4, 2, FP4>(a, gated, grid, st, ev);
-    default: return hipErrorInvalidValue;
+  if (gated) {
+    switch (cfg) {
+      case TILE_16x32_1x2_P4: return launch_one<16, 32, 1, 2, 4, true, FP4>(a, grid, st, ev);
+      case TILE_32x64_1x4_P4: return launch_one<32, 64, 1, 4, 4, true, FP4>(a, grid, st, ev);
+      case TILE_64x32_4x1_P2: return launch_one<64, 32, 4, 1, 2, true, FP4>(a, grid, st, ev);
+      case TILE_128x64_2x2_P3:
+        if constexpr (FP4) return launch_one<128, 64, 2, 2, 3, true, true>(a, grid, st, ev);
+        break;
+      case TILE_128x128_2x4_P2: return launch_one<128, 128, 2, 4, 2, true, FP4>(a, grid, st, ev);
+      default: break;
+    }
+  } else {
+    switch (cfg) {
+      case TILE_16x64_1x4_P4: return launch_one<16, 64, 1, 4, 4, false, FP4>(a, grid, st, ev);
+      case TILE_32x64_1x4_P4: return launch_one<32, 64, 1, 4, 4, false, FP4>(a, grid, st, ev);
+      case TILE_64x64_4x1_P2: return launch_one<64, 64, 4, 1, 2, false, FP4>(a, grid, st, ev);
+      case TILE_128x128_2x2_P2: return launch_one<128, 128, 2, 2, 2, false, FP4>(a, grid, st, ev);
+      default: break;
+    }
   }
+  return hipErrorInvalidValue;
 }
 
 // Host-side choice from the average rows per group (no device sync), from
@@ -488,6 +528,14 @@ static int pick_tile_cfg(bool gated, int64_t rows_per_group_hint, bool fp4) {
   if (rows_per_group_hint <= 96) return gated ? TILE_64x32_4x1_P2 : TILE_64x64_4x1_P2;
   // many rows per expert: 128 x 128 tiles (gate/up on 8 waves, two per SIMD)
   return gated ? TILE_128x128_2x4_P2 : TILE_128x128_2x2_P2;
+}
+
+// Configuration of one launch whose weights are bf16 (fp4 == false) or MXFP4
+// within a layer planned as cfg: a bf16 launch next to MXFP4 routed experts
+// (the shared expert) takes the bf16 configuration with the same row tile.
+static int launch_cfg_for_format(int cfg, bool gated, bool fp4) {
+  if (!fp4 && gated && cfg == TILE_128x64_2x2_P3) return TILE_128x128_2x4_P2;
+  return cfg;
 }
 
 GemmPlan plan_grouped_gemm(const SegShape* segs, int nseg, bool gated, int act,
@@ -507,7 +555,8 @@ GemmPlan plan_grouped_gemm(const SegShape* segs, int nseg, bool gated, int act,
   for (int l = 0; l < nl; ++l) {
     PlanLaunch& L = p.l[p.n];
     L.seg_mask = split ? (1 << l) : (nseg == 2 ? 3 : 1);
-    L.cfg = cfg;
+    L.cfg = cfg == TILE_F32 ? cfg
+                            : launch_cfg_for_format(cfg, gated, segs[split ? l : 0].wfmt != 0);
     const TileShape ls = tile_shape(L.cfg);
     L.BM = ls.BM;
     L.BN = ls.BN;

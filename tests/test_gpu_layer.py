@@ -228,6 +228,52 @@ def test_mxfp4_scale_decode_exhaustive():
     assert len(set(row[1:8].tolist())) == 7
 
 
+def _rand_mxfp4(rng, shape):
+    codes = rng.integers(0, 16, size=shape, dtype=np.uint8)
+    scales = rng.integers(118, 124, size=(shape[0], shape[1], shape[2] // 32), dtype=np.uint8)
+    packed = _pack(codes)
+    return packed, scales, _decode_bf16(packed, scales)
+
+
+def test_tile_brackets_and_weight_formats_bitwise():
+    """Every row-tile bracket of the planner (<= 2, <= 16, <= 96 and more rows
+    per expert) with MXFP4 routed experts next to a bf16 shared expert, the
+    reverse, and both MXFP4: each layer gives the bits of the all-bf16 layer
+    on the decoded weights, and a token's row is the same at every T."""
+    banner("tile brackets x weight formats")
+    E, k, D, I, Is = 4, 2, 288, 96, 64  # K % 64 == 32 in both GEMMs (trailing half step)
+    rng = np.random.default_rng(23)
+    routed = [_rand_mxfp4(rng, s) for s in ((E, I, D), (E, I, D), (E, D, I))]
+    shared = [_rand_mxfp4(rng, s) for s in ((1, Is, D), (1, Is, D), (1, D, Is))]
+
+    def fp4(m):
+        return moe.ExpertWeights(*(dev(a[0]) for a in m), *(dev(a[1]) for a in m))
+
+    def bf16(m):
+        return moe.ExpertWeights(*(dev(a[2]) for a in m))
+
+    w_router = dev(synth.normal_bf16(24, 0, E * D, 0.05).reshape(E, D))
+    layers = {
+        "bf16": moe.MoELayer(w_router, None, bf16(routed), bf16(shared), E, k, "softmax"),
+        "routed mxfp4": moe.MoELayer(w_router, None, fp4(routed), bf16(shared), E, k, "softmax"),
+        "shared mxfp4": moe.MoELayer(w_router, None, bf16(routed), fp4(shared), E, k, "softmax"),
+        "both mxfp4": moe.MoELayer(w_router, None, fp4(routed), fp4(shared), E, k, "softmax"),
+    }
+    xs = synth.normal_bf16(25, 0, 600 * D, 1.0).reshape(600, D)
+    y_all = None
+    for T in (600, 150, 20, 3, 1):  # rows per expert T*k/E = 300, 75, 10, 1.5, 0.5
+        x = dev(np.ascontiguousarray(xs[:T]))
+        ys = {name: to_np(layer.forward(x)) for name, layer in layers.items()}
+        for name, y in ys.items():
+            assert np.array_equal(y, ys["bf16"]), (T, name)
+        if y_all is None:
+            y_all = ys["bf16"]
+            assert ((y_all & 0x7F80) != 0x7F80).all()  # finite bf16
+            assert np.count_nonzero(y_all & 0x7FFF) > y_all.size // 2
+        else:
+            assert np.array_equal(ys["bf16"], y_all[:T]), T
+
+
 @pytest.mark.parametrize("cid,ntok", [(5, 12), (3, 12)])
 def test_layer_full_size_sampled(cid, ntok):
     """Full-size batch on the GPU; the oracle recomputes a sample of tokens."""
