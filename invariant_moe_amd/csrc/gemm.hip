@@ -305,29 +305,47 @@ __global__ __launch_bounds__(64 * WM * WN, 2) void k_grouped_gemm_bf16(GemmArgs 
   //   issue the loads of stage k+P (clamped to the last stage) into slot q,
   //   which stage k left at step k-1;
   //   read the second k-step of stage k (fragment set fb);
-  //   write stage k+1 from its slot into buffer (k+1)&1, whose last readers
-  //   (stage k-1) finished before the previous barrier;
-  //   MFMAs of the first k-step of stage k (fa);
+  //   MFMAs of the first k-step of stage k (fa), with the LDS writes of stage
+  //   k+1 (from its slot into buffer (k+1)&1, whose last readers, stage k-1,
+  //   finished before the previous barrier) spread between them;
   //   barrier: stage k+1 is in LDS, buffer k&1 is no longer read;
-  //   read the first k-step of stage k+1 into fa (on the last step this
-  //   reads a buffer nobody uses and fa is overwritten afterwards);
-  //   MFMAs of the second k-step of stage k (fb), covering those reads.
-  // Full groups of P steps run branch-free; the remaining nkf % P steps
-  // follow with uniform guards.
+  //   MFMAs of the second k-step of stage k (fb), with the reads of the first
+  //   k-step of stage k+1 into fa spread between them (on the last step these
+  //   read a buffer nobody uses and fa is overwritten afterwards).
+  // The scheduling groups fix that interleaving; they move instructions, never
+  // the order of the MFMAs on one accumulator.  Full groups of P steps run
+  // branch-free; the remaining nkf % P steps follow with uniform guards.
+  // Instruction counts of one step for the scheduling groups (masks of
+  // sched_group_barrier: MFMA, LDS read, LDS write).
+  constexpr int kMfmas = NMAT * NBW * TBW;                    // per k-step
+  constexpr int kFragReads = NMAT * NBW + TBW;                // per fragment set
+  constexpr int kLdsWrites = XPT + (FP4 ? 4 * QPT : WPT);     // per stage
+  constexpr int kMfmaPerWrite = kMfmas / kLdsWrites > 0 ? kMfmas / kLdsWrites : 1;
+  constexpr int kMfmaPerRead = kMfmas / kFragReads > 0 ? kMfmas / kFragReads : 1;
+  constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100, kSchedDsWrite = 0x200;
   const int nkf = K / KT;
   Frag fa, fb;
   auto step = [&](auto qc, int k) {
     constexpr int q = decltype(qc)::value;
     gload(xr[q], wr[q], sr[q], min(k + P, nkf - 1), false);
     read_frag(fb, k & 1, 1);
-    lstore(xr[(q + 1) % P], wr[(q + 1) % P], sr[(q + 1) % P], (k + 1) & 1);
     __builtin_amdgcn_sched_barrier(0);
     mma(fa);
+    lstore(xr[(q + 1) % P], wr[(q + 1) % P], sr[(q + 1) % P], (k + 1) & 1);
+    static_for<0, kLdsWrites>([&](auto) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, kMfmaPerWrite, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 1, 0);
+    });
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, kMfmas, 0);
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     read_frag(fa, (k + 1) & 1, 0);
-    __builtin_amdgcn_sched_barrier(0);
     mma(fb);
+    static_for<0, kFragReads>([&](auto) {
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, kMfmaPerRead, 1);
+    });
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, kMfmas, 1);
     __builtin_amdgcn_sched_barrier(0);
   };
   if (nkf > 0) {
