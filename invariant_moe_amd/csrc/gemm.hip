@@ -40,7 +40,16 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 constexpr int KT = 64;         // K per LDS stage (two MFMA k-steps)
-constexpr int LDK = KT + 8;    // padded LDS row (bf16 elements) -> 144 B stride
+
+// An LDS row holds one stage of one token or weight row: 64 bf16 = 128 B, no
+// padding.  Its eight 16-byte chunks are stored XOR-swizzled (chunk j of row r
+// at position j ^ (r & 7)), so that both the row-major staging writes and the
+// 16-row MFMA fragment reads spread over distinct banks.  (Measured on
+// MI355X: fragment reads over 144-byte padded rows run at 76 % of the
+// contiguous rate, over swizzled 128-byte rows at the full rate.)
+__device__ __forceinline__ int lds_off(int row, int chunk) {
+  return row * KT + ((chunk ^ (row & 7)) << 3);
+}
 
 // ---------------------------------------------------------------------------
 // Work list: one tile descriptor per workgroup, written on the device from the
@@ -112,17 +121,26 @@ __global__ __launch_bounds__(64 * WM * WN, 2) void k_grouped_gemm_bf16(GemmArgs 
   constexpr int WPT = (WCH + NT - 1) / NT;
   constexpr int QPT = (QCH + NT - 1) / NT;
   constexpr int WQ = FP4 ? QPT : WPT;
-  constexpr int BUF = (BM + NMAT * BN) * LDK;  // bf16 elements of one LDS stage
+  constexpr int BUF = (BM + NMAT * BN) * KT;  // bf16 elements of one LDS stage
   __shared__ __align__(16) unsigned char smem[2 * BUF * 2];
 
   TileInfo ti;
   if (!read_tile(args, BM, ti)) return;
-  uint16_t* lds = reinterpret_cast<uint16_t*>(smem);  // [2][BM + NMAT*BN][LDK]
+  uint16_t* lds = reinterpret_cast<uint16_t*>(smem);  // [2][BM + NMAT*BN][KT], swizzled
   const GemmSeg& s = args.seg[ti.seg];
   const int K = s.K, N = s.N;
   constexpr bool fp4 = FP4;  // weight format of this instantiation (the launcher splits segments)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave % WM, wn = wave / WM;
+  // Wave w takes row block wm = w / WN and feature block wn = w % WN.  In
+  // 128-row tiles a wave whose rows all lie past the tile's valid rows does no
+  // MFMA work (only its share of the loads and LDS writes); waves are dealt to
+  // the four SIMDs round-robin, so with WN a multiple of 4 the waves of one
+  // SIMD hold different row blocks and a half-empty tile frees half of every
+  // SIMD.  (Measured: 9-10 % off the MXFP4 expert GEMMs at 64 rows per
+  // expert; in 64-row tiles the skip costs more than it saves.)  Row blocks
+  // do not change any element's chain.
+  const int wm = wave / WN, wn = wave % WN;
+  const bool active = BM < 128 || wm * TBW * 16 < ti.rows;  // uniform per wave
 
   // Token rows of this thread's chunks (rows clamped into the tile).  With a
   // row index the indices are loaded here, before the weight prefetch below,
@@ -235,19 +253,19 @@ __global__ __launch_bounds__(64 * WM * WN, 2) void k_grouped_gemm_bf16(GemmArgs 
   auto lstore = [&](const uint4 (&xq)[XPT], const uint4 (&wq)[WQ], const uint32_t (&sq)[QPT],
                     int buf) {
     uint16_t* Xs = lds + buf * BUF;
-    uint16_t* Ws = Xs + BM * LDK;
+    uint16_t* Ws = Xs + BM * KT;
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
       const int c = tid + i * NT;
       if (XCH % NT == 0 || c < XCH)
-        *reinterpret_cast<uint4*>(&Xs[(c / (KT / 8)) * LDK + (c % (KT / 8)) * 8]) = xq[i];
+        *reinterpret_cast<uint4*>(&Xs[lds_off(c / (KT / 8), c % (KT / 8))]) = xq[i];
     }
     if constexpr (!fp4) {
 #pragma unroll
       for (int i = 0; i < WPT; ++i) {
         const int c = tid + i * NT;
         if (WCH % NT == 0 || c < WCH)
-          *reinterpret_cast<uint4*>(&Ws[(c / (KT / 8)) * LDK + (c % (KT / 8)) * 8]) = wq[i];
+          *reinterpret_cast<uint4*>(&Ws[lds_off(c / (KT / 8), c % (KT / 8))]) = wq[i];
       }
     } else {
 #pragma unroll
@@ -256,11 +274,11 @@ __global__ __launch_bounds__(64 * WM * WN, 2) void k_grouped_gemm_bf16(GemmArgs 
         if (QCH % NT == 0 || c < QCH) {
           uint32_t o[16];
           decode_mxfp4_32(wq[i], sq[i], o);
-          uint4* dst = reinterpret_cast<uint4*>(&Ws[(c / 2) * LDK + (c % 2) * 32]);
-          dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-          dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
-          dst[2] = make_uint4(o[8], o[9], o[10], o[11]);
-          dst[3] = make_uint4(o[12], o[13], o[14], o[15]);
+          const int row = c / 2, ch = (c % 2) * 4;  // 32 k values = chunks ch..ch+3
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<uint4*>(&Ws[lds_off(row, ch + j)]) =
+                make_uint4(o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]);
         }
       }
     }
@@ -275,18 +293,21 @@ __global__ __launch_bounds__(64 * WM * WN, 2) void k_grouped_gemm_bf16(GemmArgs 
   };
   auto read_frag = [&](Frag& f, int buf, int ks) {
     const uint16_t* Xs = lds + buf * BUF;
-    const uint16_t* Ws = Xs + BM * LDK;
+    const uint16_t* Ws = Xs + BM * KT;
+    // Rows n and r below are 16-row block bases plus lane & 15, so row & 7 is
+    // lane & 7 and the swizzled chunk is the same for every block.
+    const int sw = ((ks * 4 + (lane >> 4)) ^ (lane & 7)) << 3;
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
       for (int nb = 0; nb < NBW; ++nb) {
         const int n = m * BN + (wn * NBW + nb) * 16 + (lane & 15);
-        f.a[m][nb] = *reinterpret_cast<const bf16x8_t*>(&Ws[n * LDK + ks * 32 + 8 * (lane >> 4)]);
+        f.a[m][nb] = *reinterpret_cast<const bf16x8_t*>(&Ws[n * KT + sw]);
       }
 #pragma unroll
     for (int tb = 0; tb < TBW; ++tb) {
       const int r = (wm * TBW + tb) * 16 + (lane & 15);
-      f.b[tb] = *reinterpret_cast<const bf16x8_t*>(&Xs[r * LDK + ks * 32 + 8 * (lane >> 4)]);
+      f.b[tb] = *reinterpret_cast<const bf16x8_t*>(&Xs[r * KT + sw]);
     }
   };
   auto mma = [&](const Frag& f) {
@@ -365,12 +386,27 @@ __global__ __launch_bounds__(64 * WM * WN, 2) void k_grouped_gemm_bf16(GemmArgs 
     for (int q = 0; q < P; ++q) gload_x(xr[q], min(q, nkf - 1), false);
     lstore(xr[0], wr[0], sr[0], 0);
     __syncthreads();
-    read_frag(fa, 0, 0);
     const int nfull = nkf / P * P;
-    for (int kt = 0; kt < nfull; kt += P) static_for<0, P>([&](auto qc) { step(qc, kt + qc); });
-    static_for<0, P>([&](auto qc) {
-      if (nfull + qc < nkf) step(qc, nfull + qc);
-    });
+    if (active) {
+      read_frag(fa, 0, 0);
+      for (int kt = 0; kt < nfull; kt += P) static_for<0, P>([&](auto qc) { step(qc, kt + qc); });
+      static_for<0, P>([&](auto qc) {
+        if (nfull + qc < nkf) step(qc, nfull + qc);
+      });
+    } else {
+      // Same loads, LDS writes and barriers as step(), without fragments.
+      auto idle_step = [&](auto qc, int k) {
+        constexpr int q = decltype(qc)::value;
+        gload(xr[q], wr[q], sr[q], min(k + P, nkf - 1), false);
+        lstore(xr[(q + 1) % P], wr[(q + 1) % P], sr[(q + 1) % P], (k + 1) & 1);
+        __syncthreads();
+      };
+      for (int kt = 0; kt < nfull; kt += P)
+        static_for<0, P>([&](auto qc) { idle_step(qc, kt + qc); });
+      static_for<0, P>([&](auto qc) {
+        if (nfull + qc < nkf) idle_step(qc, nfull + qc);
+      });
+    }
   }
   // Trailing k-step: the last 32 of K when K % 64 == 32, and a step over zero
   // operands otherwise.  Running it unconditionally keeps one chain for every
@@ -379,8 +415,10 @@ __global__ __launch_bounds__(64 * WM * WN, 2) void k_grouped_gemm_bf16(GemmArgs 
   gload(xr[0], wr[0], sr[0], nkf, true);
   lstore(xr[0], wr[0], sr[0], nkf & 1);
   __syncthreads();
-  read_frag(fa, nkf & 1, 0);
-  mma(fa);
+  if (active) {
+    read_frag(fa, nkf & 1, 0);
+    mma(fa);
+  }
 
   // epilogue: lane holds features n = base + 4*(lane/16) + i (i = 0..3) of
   // token row base + lane%16 -> one 8-byte store of 4 bf16.
@@ -479,7 +517,7 @@ enum TileCfg {
   TILE_32x64_1x4_P4,
   TILE_64x32_4x1_P2,      // tens of rows per expert
   TILE_64x64_4x1_P2,
-  TILE_128x64_2x2_P3,     // MXFP4 weights with tens of rows per expert
+  TILE_128x64_2x2_P2,     // MXFP4 weights with tens of rows per expert
   TILE_128x128_2x2_P2,    // prefill
   TILE_128x128_2x4_P2,    // prefill gate/up: 8 waves, two per SIMD
   TILE_COUNT,
@@ -497,7 +535,7 @@ static TileShape tile_shape(int cfg) {
     case TILE_32x64_1x4_P4: return {32, 64};
     case TILE_64x32_4x1_P2: return {64, 32};
     case TILE_64x64_4x1_P2: return {64, 64};
-    case TILE_128x64_2x2_P3: return {128, 64};
+    case TILE_128x64_2x2_P2: return {128, 64};
     case TILE_128x128_2x2_P2: return {128, 128};
     case TILE_128x128_2x4_P2: return {128, 128};
     default: return {16, 16};  // TILE_F32
@@ -517,8 +555,8 @@ static hipError_t launch_tile_cfg(int cfg, const GemmArgs& a, bool gated, int64_
       case TILE_16x32_1x2_P4: return launch_one<16, 32, 1, 2, 4, true, FP4>(a, grid, st, ev);
       case TILE_32x64_1x4_P4: return launch_one<32, 64, 1, 4, 4, true, FP4>(a, grid, st, ev);
       case TILE_64x32_4x1_P2: return launch_one<64, 32, 4, 1, 2, true, FP4>(a, grid, st, ev);
-      case TILE_128x64_2x2_P3:
-        if constexpr (FP4) return launch_one<128, 64, 2, 2, 3, true, true>(a, grid, st, ev);
+      case TILE_128x64_2x2_P2:
+        if constexpr (FP4) return launch_one<128, 64, 2, 2, 2, true, true>(a, grid, st, ev);
         break;
       case TILE_128x128_2x4_P2: return launch_one<128, 128, 2, 4, 2, true, FP4>(a, grid, st, ev);
       default: break;
@@ -542,7 +580,7 @@ static int pick_tile_cfg(bool gated, int64_t rows_per_group_hint, bool fp4) {
   if (rows_per_group_hint <= 16) return TILE_32x64_1x4_P4;
   // MXFP4 weights: the decode in the LDS staging favours 128-row tiles
   // (each decoded weight serves more token rows)
-  if (fp4 && rows_per_group_hint <= 96) return gated ? TILE_128x64_2x2_P3 : TILE_128x128_2x2_P2;
+  if (fp4 && rows_per_group_hint <= 96) return gated ? TILE_128x64_2x2_P2 : TILE_128x128_2x2_P2;
   if (rows_per_group_hint <= 96) return gated ? TILE_64x32_4x1_P2 : TILE_64x64_4x1_P2;
   // many rows per expert: 128 x 128 tiles (gate/up on 8 waves, two per SIMD)
   return gated ? TILE_128x128_2x4_P2 : TILE_128x128_2x2_P2;
@@ -552,7 +590,7 @@ static int pick_tile_cfg(bool gated, int64_t rows_per_group_hint, bool fp4) {
 // within a layer planned as cfg: a bf16 launch next to MXFP4 routed experts
 // (the shared expert) takes the bf16 configuration with the same row tile.
 static int launch_cfg_for_format(int cfg, bool gated, bool fp4) {
-  if (!fp4 && gated && cfg == TILE_128x64_2x2_P3) return TILE_128x128_2x4_P2;
+  if (!fp4 && gated && cfg == TILE_128x64_2x2_P2) return TILE_128x128_2x4_P2;
   return cfg;
 }
 
