@@ -9,15 +9,21 @@
 
 namespace moe {
 
+// Mask words (and their prefixes) are kept in LDS when the mask has at most
+// this many words (E * ceil(T / 64)); larger masks go through wprefix.
+constexpr int kPermLdsWords = 4096;
+
 template <int NT>
 struct PermuteLds {
   int soff[MOE_MAX_EXPERTS + 1];
   int mpre[MOE_MAX_EXPERTS + 1];
   int wsum[2 * (NT / 64)];
   int omap[kTileOwnerMax];
+  unsigned long long wmask[kPermLdsWords];
+  int wpre[kPermLdsWords];
 };
 
-// counts, offsets, per-(expert, block) prefixes, the tile tables of the
+// counts, offsets, per-(expert, word) prefixes, the tile tables of the
 // grouped GEMMs that follow, then the scatter.  Run by nwg workgroups of NT
 // threads: each computes the counts and prefixes itself (all get the same
 // values), then writes its share of the tables and of the scatter.
@@ -30,23 +36,68 @@ __device__ void permute_core(const int32_t* __restrict__ topk_idx, int64_t T, in
                              PermuteLds<NT>& L, int wg, int nwg) {
   const int BM = jobs.n > 0 ? jobs.BM : 1;
   const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += NT) {
-    int c = 0;
-    const uint64_t* me = mask + (int64_t)e * W;
-    int32_t* pe = wprefix + (int64_t)e * W;
-    for (int b0 = 0; b0 < (int)W; b0 += 8) {  // eight mask words in flight
+  const int Wi = (int)W;
+  const bool in_lds = (int64_t)E * W <= kPermLdsWords;
+
+  // The scatter's first four pairs per thread do not depend on anything
+  // below: their expert ids are loaded first.  Indices fit in 32 bits
+  // (T * k < 2^31).
+  const unsigned R = (unsigned)(T * k), uk = (unsigned)k;
+  const unsigned pstart = (unsigned)wg * 4 * NT + tid, pstep = (unsigned)nwg * 4 * NT;
+  int efirst[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const unsigned p = pstart + u * NT;
+    efirst[u] = p < R ? topk_idx[p] : -1;
+  }
+
+  // Per-(expert, word) exclusive prefixes of the mask popcounts.  tpe
+  // consecutive threads share an expert, each taking a run of S words (all
+  // its loads in flight), then scan their run totals with shuffles.
+  int tpe = 1;
+  while (tpe < 64 && 2 * tpe * E <= NT) tpe *= 2;
+  const int e1 = tid / tpe, s1 = tid % tpe;
+  const int S = (Wi + tpe - 1) / tpe;
+  const int b0 = min(s1 * S, Wi), b1 = min(b0 + S, Wi);
+  int run = 0;
+  if (e1 < E) {
+    const uint64_t* me = mask + (int64_t)e1 * W;
+    for (int b = b0; b < b1; b += 8) {
       uint64_t v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = b0 + u < W ? me[b0 + u] : 0ull;
+      for (int u = 0; u < 8; ++u) v[u] = b + u < b1 ? me[b + u] : 0ull;
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        if (b0 + u < W) pe[b0 + u] = c;  // the same value from every workgroup
-        c += __popcll(v[u]);
+        if (in_lds && b + u < b1) L.wmask[e1 * Wi + b + u] = v[u];
+        run += __popcll(v[u]);
       }
     }
-    if (wg == 0) counts[e] = c;
-    L.soff[e] = c;
-    L.mpre[e] = (c + BM - 1) / BM;
+  }
+  int incl = run;  // every thread takes part in the shuffles (tpe is uniform)
+  for (int m = 1; m < tpe; m <<= 1) {
+    const int o = __shfl_up(incl, m, tpe);
+    if (s1 >= m) incl += o;
+  }
+  if (e1 < E) {
+    int pre = incl - run;
+    if (in_lds) {
+      for (int b = b0; b < b1; ++b) {
+        L.wpre[e1 * Wi + b] = pre;
+        pre += __popcll(L.wmask[e1 * Wi + b]);
+      }
+    } else {
+      const uint64_t* me = mask + (int64_t)e1 * W;
+      int32_t* pe = wprefix + (int64_t)e1 * W;
+      for (int b = b0; b < b1; ++b) {
+        pe[b] = pre;  // the same value from every workgroup
+        pre += __popcll(me[b]);
+      }
+    }
+    if (s1 == tpe - 1) {
+      if (wg == 0) counts[e1] = incl;
+      L.soff[e1] = incl;
+      L.mpre[e1] = (incl + BM - 1) / BM;
+    }
   }
   __syncthreads();
   tile_scan2<NT>(L.soff, L.mpre, E, L.wsum);
@@ -56,26 +107,29 @@ __device__ void permute_core(const int32_t* __restrict__ topk_idx, int64_t T, in
     const bool map = build_tile_owner<NT>(L.mpre, E, L.omap);
     build_tile_tables<NT>(jobs, L.soff, L.mpre, map ? L.omap : nullptr, E, wg, nwg);
   }
-  // wprefix written above by this workgroup is visible after the barriers.
-  // Four pairs per thread per round, their loads issued together; indices
-  // fit in 32 bits (T * k < 2^31).
-  const unsigned R = (unsigned)(T * k), uk = (unsigned)k;
-  for (unsigned p0 = (unsigned)wg * 4 * NT + tid; p0 < R; p0 += (unsigned)nwg * 4 * NT) {
+  // The LDS words and prefixes, or the wprefix entries this workgroup wrote,
+  // are visible after the barriers above.  Four pairs per thread per round.
+  for (unsigned p0 = pstart; p0 < R; p0 += pstep) {
     int e[4];
     uint64_t word[4];
     int32_t pre_b[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const unsigned p = p0 + u * NT;
-      e[u] = p < R ? topk_idx[p] : -1;
+      e[u] = p0 == pstart ? efirst[u] : (p < R ? topk_idx[p] : -1);
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const unsigned p = p0 + u * NT;
       const bool valid = p < R && e[u] >= 0 && e[u] < E;
       const int64_t at = valid ? (int64_t)e[u] * W + ((p / uk) >> 6) : 0;
-      word[u] = valid ? mask[at] : 0ull;
-      pre_b[u] = valid ? wprefix[at] : 0;
+      if (in_lds) {
+        word[u] = valid ? L.wmask[at] : 0ull;
+        pre_b[u] = valid ? L.wpre[at] : 0;
+      } else {
+        word[u] = valid ? mask[at] : 0ull;
+        pre_b[u] = valid ? wprefix[at] : 0;
+      }
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
