@@ -10,7 +10,7 @@
 namespace moe {
 
 // Mask words (and their prefixes) are kept in LDS when the mask has at most
-// this many words (E * ceil(T / 64)); larger masks go through wprefix.
+// this many words (E * ceil(T / 64)); otherwise prefixes go through wprefix.
 constexpr int kPermLdsWords = 4096;
 
 template <int NT>
@@ -37,7 +37,10 @@ __device__ void permute_core(const int32_t* __restrict__ topk_idx, int64_t T, in
   const int BM = jobs.n > 0 ? jobs.BM : 1;
   const int tid = threadIdx.x;
   const int Wi = (int)W;
-  const bool in_lds = (int64_t)E * W <= kPermLdsWords;
+  // LDS path for small masks of several words per expert (measured: 0.5 us
+  // faster at 512 tokens x 64 experts, slower with a single word, and the
+  // one-thread-per-expert walk is faster for masks past the LDS limit).
+  const bool in_lds = W >= 2 && (int64_t)E * W <= kPermLdsWords;
 
   // The scatter's first four pairs per thread do not depend on anything
   // below: their expert ids are loaded first.  Indices fit in 32 bits
@@ -51,52 +54,67 @@ __device__ void permute_core(const int32_t* __restrict__ topk_idx, int64_t T, in
     efirst[u] = p < R ? topk_idx[p] : -1;
   }
 
-  // Per-(expert, word) exclusive prefixes of the mask popcounts.  tpe
-  // consecutive threads share an expert, each taking a run of S words (all
-  // its loads in flight), then scan their run totals with shuffles.
-  int tpe = 1;
-  while (tpe < 64 && 2 * tpe * E <= NT) tpe *= 2;
-  const int e1 = tid / tpe, s1 = tid % tpe;
-  const int S = (Wi + tpe - 1) / tpe;
-  const int b0 = min(s1 * S, Wi), b1 = min(b0 + S, Wi);
-  int run = 0;
-  if (e1 < E) {
-    const uint64_t* me = mask + (int64_t)e1 * W;
-    for (int b = b0; b < b1; b += 8) {
-      uint64_t v[8];
+  // Per-(expert, word) exclusive prefixes of the mask popcounts.
+  if (in_lds) {
+    // tpe consecutive threads share an expert, each taking a run of S words
+    // (all its loads in flight), then scan their run totals with shuffles;
+    // words and prefixes stay in LDS.
+    int tpe = 1;
+    while (tpe < 64 && 2 * tpe * E <= NT) tpe *= 2;
+    const int e1 = tid / tpe, s1 = tid % tpe;
+    const int S = (Wi + tpe - 1) / tpe;
+    const int b0 = min(s1 * S, Wi), b1 = min(b0 + S, Wi);
+    int run = 0;
+    if (e1 < E) {
+      const uint64_t* me = mask + (int64_t)e1 * W;
+      for (int b = b0; b < b1; b += 8) {
+        uint64_t v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = b + u < b1 ? me[b + u] : 0ull;
+        for (int u = 0; u < 8; ++u) v[u] = b + u < b1 ? me[b + u] : 0ull;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (in_lds && b + u < b1) L.wmask[e1 * Wi + b + u] = v[u];
-        run += __popcll(v[u]);
+        for (int u = 0; u < 8; ++u) {
+          if (b + u < b1) L.wmask[e1 * Wi + b + u] = v[u];
+          run += __popcll(v[u]);
+        }
       }
     }
-  }
-  int incl = run;  // every thread takes part in the shuffles (tpe is uniform)
-  for (int m = 1; m < tpe; m <<= 1) {
-    const int o = __shfl_up(incl, m, tpe);
-    if (s1 >= m) incl += o;
-  }
-  if (e1 < E) {
-    int pre = incl - run;
-    if (in_lds) {
+    int incl = run;  // every thread takes part in the shuffles (tpe is uniform)
+    for (int m = 1; m < tpe; m <<= 1) {
+      const int o = __shfl_up(incl, m, tpe);
+      if (s1 >= m) incl += o;
+    }
+    if (e1 < E) {
+      int pre = incl - run;
       for (int b = b0; b < b1; ++b) {
         L.wpre[e1 * Wi + b] = pre;
         pre += __popcll(L.wmask[e1 * Wi + b]);
       }
-    } else {
-      const uint64_t* me = mask + (int64_t)e1 * W;
-      int32_t* pe = wprefix + (int64_t)e1 * W;
-      for (int b = b0; b < b1; ++b) {
-        pe[b] = pre;  // the same value from every workgroup
-        pre += __popcll(me[b]);
+      if (s1 == tpe - 1) {
+        if (wg == 0) counts[e1] = incl;
+        L.soff[e1] = incl;
+        L.mpre[e1] = (incl + BM - 1) / BM;
       }
     }
-    if (s1 == tpe - 1) {
-      if (wg == 0) counts[e1] = incl;
-      L.soff[e1] = incl;
-      L.mpre[e1] = (incl + BM - 1) / BM;
+  } else {
+    // One thread per expert walks its words, eight loads in flight, writing
+    // the prefixes to wprefix (the same values from every workgroup).
+    for (int e = tid; e < E; e += NT) {
+      int c = 0;
+      const uint64_t* me = mask + (int64_t)e * W;
+      int32_t* pe = wprefix + (int64_t)e * W;
+      for (int b0 = 0; b0 < Wi; b0 += 8) {
+        uint64_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = b0 + u < Wi ? me[b0 + u] : 0ull;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (b0 + u < Wi) pe[b0 + u] = c;
+          c += __popcll(v[u]);
+        }
+      }
+      if (wg == 0) counts[e] = c;
+      L.soff[e] = c;
+      L.mpre[e] = (c + BM - 1) / BM;
     }
   }
   __syncthreads();
