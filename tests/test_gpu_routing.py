@@ -29,8 +29,8 @@ def _routing_case(cfg, T=None, offset=0):
     return to_np(idx), to_np(w), ref_idx, ref_w
 
 
-@pytest.mark.parametrize("cid,T", [(1, None), (2, None), (2, 1), (2, 33), (4, 64), (4, 1),
-                                   (5, None), (3, 300)])
+@pytest.mark.parametrize("cid,T", [(1, None), (1, 3), (1, 10), (2, None), (2, 1), (2, 12),
+                                   (2, 33), (4, 64), (4, 1), (4, 9), (5, None), (3, 300)])
 def test_router_bitwise(cid, T):
     cfg = synth.CONFIGS[cid]
     banner(f"router cfg{cid} T={T}")
