@@ -115,6 +115,31 @@ def test_fp32_stage_parity():
                           oracle.combine(o_ref, idx, w, pair_row, None, cfg.T, cfg.k, cfg.D).view(np.uint32))
 
 
+@pytest.mark.parametrize("act", ["bf16", "f32"])
+def test_combine_many_slots_bitwise(act):
+    """Combine with k = 9, 17 and 32 slots (several batches of eight rows,
+    clamped tail slots), ragged T, two row widths, with and without a shared
+    expert: bit-exact against the oracle's fixed-order combine."""
+    banner(f"combine many slots {act}")
+    rng = np.random.default_rng(31)
+    E = 40
+    for T, k, D in ((37, 9, 256), (5, 17, 1056), (3, 32, 1056)):
+        idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+        w = rng.random((T, k), dtype=np.float32)
+        _, _, _, pair_row = oracle.permute(idx, E)
+        if act == "bf16":
+            o = synth.normal_bf16(32, 0, T * k * D, 1.0).reshape(T * k, D)
+            sh = synth.normal_bf16(33, 0, T * D, 1.0).reshape(T, D)
+        else:
+            o = rng.standard_normal((T * k, D), dtype=np.float32)
+            sh = rng.standard_normal((T, D), dtype=np.float32)
+        for shared in (sh, None):
+            y = to_np(moe.combine(dev(o), dev(idx), dev(w), dev(pair_row),
+                                  None if shared is None else dev(shared)))
+            ref = oracle.combine(o, idx, w, pair_row, shared, T, k, D)
+            assert np.array_equal(y.view(np.uint8), ref.view(np.uint8)), (T, k, D, shared is None)
+
+
 def test_batch_invariance_small_layer():
     """Every token's output row is bitwise identical for batch sizes 1..64, for
     shuffled batches, and inside the full 512-token batch (recipe 2 weights;
