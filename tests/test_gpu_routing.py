@@ -111,6 +111,25 @@ def test_router_ties_and_edges():
     assert np.array_equal(to_np(w).view(np.uint32), ref_w.view(np.uint32))
 
 
+@pytest.mark.parametrize("T,E,k", [(9, 300, 8), (20, 1000, 32), (3, 1024, 1)])
+@pytest.mark.parametrize("mode", ["softmax", "sigmoid"])
+def test_router_many_experts_bitwise(T, E, k, mode):
+    """Top-k over 8 and 16 keys per lane (E up to the 1024 limit, k up to 32),
+    with and without a bias: indices and weights bit-exact."""
+    banner(f"router E={E} k={k} {mode}")
+    D = 256
+    x = synth.normal_bf16(40, 0, T * D, 1.0).reshape(T, D)
+    wr = synth.normal_bf16(41, 0, E * D, 0.05).reshape(E, D)
+    logits = oracle.router_logits(x, wr)
+    rng = np.random.default_rng(E + k)
+    for bias in (None, (rng.standard_normal(E) * 0.01).astype(np.float32)):
+        idx, w = moe.router_topk(dev(x), dev(wr), None if bias is None else dev(bias), None, E, k,
+                                 mode)
+        ref_idx, ref_w = oracle.route(logits, bias, None, T, E, k, mode)
+        assert np.array_equal(to_np(idx), ref_idx)
+        assert np.array_equal(to_np(w).view(np.uint32), ref_w.view(np.uint32))
+
+
 @pytest.mark.parametrize("T,E,k", [(1, 8, 2), (64, 64, 6), (65, 64, 6), (300, 256, 8),
                                    (4096, 256, 8), (1000, 1024, 32), (7, 3, 3), (130, 1, 1)])
 def test_permute_bitwise(T, E, k):
