@@ -115,6 +115,33 @@ def test_fp32_stage_parity():
                           oracle.combine(o_ref, idx, w, pair_row, None, cfg.T, cfg.k, cfg.D).view(np.uint32))
 
 
+def test_grouped_gemm_past_owner_map():
+    """More than 8192 row tiles (1.1 M rows in 128-row tiles): the tile tables
+    find each tile's expert by binary search instead of the LDS owner map.
+    Sampled rows match the oracle; the first rows match a small run bitwise."""
+    banner("grouped GEMM, 1.1 M rows")
+    E, D, I = 3, 64, 32
+    sizes = np.array([400_000, 1, 700_123], dtype=np.int64)
+    R = int(sizes.sum())
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    rng = np.random.default_rng(51)
+    x = synth.normal_bf16(52, 0, R * D, 1.0).reshape(R, D)
+    mats = [synth.normal_bf16(53 + i, 0, E * r * c, 0.1).reshape(E, r, c)
+            for i, (r, c) in enumerate(((I, D), (I, D), (D, I)))]
+    w = moe.ExpertWeights(*(dev(m) for m in mats))
+    out = to_np(moe.grouped_swiglu(dev(x), None, dev(offsets), R, E, w))
+    rows = np.sort(np.concatenate([rng.choice(R, 300, replace=False), [0, R - 1, 400_000]]))
+    for e in range(E):
+        sel = rows[(rows >= offsets[e]) & (rows < offsets[e + 1])]
+        if len(sel):
+            ref = oracle.expert_ffn(np.ascontiguousarray(x[sel]), mats[0][e], mats[1][e],
+                                    mats[2][e], "bf16")
+            assert rel_l2(out[sel], ref) <= 2e-3, e
+    small = to_np(moe.grouped_swiglu(dev(np.ascontiguousarray(x[:1000])), None,
+                                     dev(np.array([0, 1000, 1000, 1000], np.int32)), 1000, E, w))
+    assert np.array_equal(small, out[:1000])
+
+
 @pytest.mark.parametrize("act", ["bf16", "f32"])
 def test_combine_many_slots_bitwise(act):
     """Combine with k = 9, 17 and 32 slots (several batches of eight rows,
