@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "liboracle.so")
 ACT = {"f32": 0, "bf16": 1}
 WDT = {"f32": 0, "bf16": 1, "mxfp4": 2}
 ROUTE = {"softmax": 0, "sigmoid": 1, "hash": 2}
+GLU = {"swiglu": 0, "clamp": 1, "situ": 2}
 
 _lib = None
 
@@ -40,6 +41,8 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
         L.orc_exp.argtypes, L.orc_exp.restype = [f32], f32
+        L.orc_glu_value.argtypes = [ctypes.c_double, ctypes.c_double, i32]
+        L.orc_glu_value.restype = ctypes.c_double
         L.orc_sigmoid.argtypes, L.orc_sigmoid.restype = [f32], f32
         L.orc_bf16_from_f64.argtypes, L.orc_bf16_from_f64.restype = [ctypes.c_double], ctypes.c_uint16
         L.orc_bf16_from_f32.argtypes, L.orc_bf16_from_f32.restype = [f32], ctypes.c_uint16
@@ -54,10 +57,11 @@ def lib():
         L.orc_route.restype = i32
         L.orc_permute.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp]
         L.orc_permute.restype = i32
-        L.orc_expert_ffn.argtypes = [vp, i32, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.orc_expert_ffn.argtypes = [vp, i32, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                     i32]
         L.orc_combine.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i32, vp]
         L.orc_layer_forward.argtypes = [vp, i32, vp, vp, vp, ctypes.POINTER(_Experts), vp, vp, vp,
-                                        i64, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp]
+                                        i64, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, i32]
         L.orc_layer_forward.restype = i32
         L.orc_num_threads.restype = i32
         _lib = L
@@ -81,6 +85,11 @@ def exp(x: float) -> float:
 
 def sigmoid(x: float) -> float:
     return lib().orc_sigmoid(x)
+
+
+def glu_value(g: float, u: float, glu: str = "swiglu") -> float:
+    """Gated activation of one (gate, up) pair in double (see glu_value in oracle.cpp)."""
+    return lib().orc_glu_value(g, u, GLU[glu])
 
 
 def exp_array(x: np.ndarray) -> np.ndarray:
@@ -136,8 +145,9 @@ def permute(topk_idx: np.ndarray, E: int):
     return counts, offsets, row_token, pair_row
 
 
-def expert_ffn(x_rows: np.ndarray, gate, up, down, wdtype: str, want_h=False):
-    """One expert over M rows.  For mxfp4 each weight is a (codes, scales) pair."""
+def expert_ffn(x_rows: np.ndarray, gate, up, down, wdtype: str, want_h=False, glu="swiglu"):
+    """One expert over M rows.  For mxfp4 each weight is a (codes, scales) pair.
+    glu: "swiglu", "clamp" or "situ" (the gated activation)."""
     M, D = x_rows.shape
     act = act_name(x_rows)
     if wdtype == "mxfp4":
@@ -150,7 +160,7 @@ def expert_ffn(x_rows: np.ndarray, gate, up, down, wdtype: str, want_h=False):
     out = np.empty((M, D), dtype=x_rows.dtype)
     h = np.empty((M, I), dtype=x_rows.dtype) if want_h else None
     lib().orc_expert_ffn(_p(x_rows), ACT[act], M, D, I, WDT[wdtype], _p(g), _p(u), _p(d),
-                         _p(gs), _p(us), _p(ds), _p(out), _p(h))
+                         _p(gs), _p(us), _p(ds), _p(out), _p(h), GLU[glu])
     return (out, h) if want_h else out
 
 
@@ -162,9 +172,10 @@ def combine(expert_out, topk_idx, topk_w, pair_row, shared_out, T, k, D):
 
 
 def layer_forward(x, token_ids, w_router, bias, experts: dict, shared, T, D, E, k, I,
-                  I_shared, mode, wdtype):
+                  I_shared, mode, wdtype, glu="swiglu"):
     """experts: {e: (gate, up, down)} (entries may be missing for untouched experts;
     mxfp4 entries are (codes, scales) pairs).  shared: (gate, up, down) or None.
+    glu: the gated activation of every expert FFN ("swiglu", "clamp", "situ").
     Returns (y, topk_idx, topk_w, macs[3])."""
     arr = ctypes.c_void_p * E
     g, u, d = arr(), arr(), arr()
@@ -191,7 +202,7 @@ def layer_forward(x, token_ids, w_router, bias, experts: dict, shared, T, D, E, 
     rc = lib().orc_layer_forward(_p(x), ACT[act_name(x)], _p(token_ids), _p(w_router), _p(bias),
                                  ctypes.byref(ex), _p(sg), _p(su), _p(sd), T, D, E, k, I,
                                  I_shared if shared is not None else 0, ROUTE[mode], _p(y),
-                                 _p(idx), _p(w), _p(macs))
+                                 _p(idx), _p(w), _p(macs), GLU[glu])
     if rc != 0:
         raise ValueError(f"orc_layer_forward rc={rc}")
     return y, idx, w, macs

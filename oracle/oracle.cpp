@@ -42,6 +42,8 @@
  *  - rounding points: h, o, s rounded to the activation type (bf16 RNE or
  *    fp32), combine in fp32 in ascending expert id with fmaf, shared added
  *    last, one final rounding.
+ *  - gated-activation variants (glu_value below) replace SiLU(g) * u in every
+ *    SwiGLU of the layer, routed experts and the shared expert alike.
  */
 #include <algorithm>
 #include <cmath>
@@ -231,12 +233,38 @@ void route_token(const float* logits, const float* bias, int32_t tid, int E, int
   }
 }
 
+/* Gated activation a(g, u) of the expert FFN from the gate branch g = W_g x
+ * and the up branch u = W_u x, in double:
+ *  GLU_SWIGLU  SiLU(g) * u, SiLU(g) = g * sigmoid(g)        ([DS] 6.5; [LD] GLU branches)
+ *  GLU_CLAMP   SiLU(min(g, 10)) * min(max(u, -10), 10)      ([DS] 6.5, the clamped SwiGLU:
+ *              the gate branch is capped from above only, the up branch on both sides)
+ *  GLU_SITU    [b1 tanh(g / b1) * sigmoid(g)] * [b2 tanh(u / b2)], b1 = 4 (gate), b2 = 25
+ *              (up) ([LD] "SiTU-GLU": a scaled-tanh soft cap on each branch; the
+ *              sigmoid takes the uncapped gate value)
+ * A NaN branch value gives NaN (the comparisons below keep it). */
+enum { GLU_SWIGLU = 0, GLU_CLAMP = 1, GLU_SITU = 2 };
+const double kClampGate = 10.0, kClampUp = 10.0;
+const double kSituGate = 4.0, kSituUp = 25.0;
+
+double glu_value(double g, double u, int glu) {
+  if (glu == GLU_CLAMP) {
+    g = g > kClampGate ? kClampGate : g;
+    u = u > kClampUp ? kClampUp : (u < -kClampUp ? -kClampUp : u);
+    return g / (1.0 + std::exp(-g)) * u;
+  }
+  if (glu == GLU_SITU) {
+    const double gate = kSituGate * std::tanh(g / kSituGate) * (1.0 / (1.0 + std::exp(-g)));
+    return gate * (kSituUp * std::tanh(u / kSituUp));
+  }
+  return g / (1.0 + std::exp(-g)) * u;  // SiLU(g) * u
+}
+
 /* SwiGLU FFN of M rows with one expert's weights (double accumulation, the
  * method's rounding points).  x_rows [M,D] act; out [M,D] act; h_out [M,I] act. */
 void expert_ffn(const void* x_rows, int act, int64_t M, int D, int I,
                 const std::vector<double>& Wg, const std::vector<double>& Wu,
                 const std::vector<double>& Wd, void* out, void* h_out,
-                uint64_t* macs) {
+                uint64_t* macs, int glu) {
   std::vector<double> h((size_t)(M * I));
 #pragma omp parallel for schedule(dynamic, 4)
   for (int64_t ri = 0; ri < M * I; ++ri) {
@@ -247,7 +275,7 @@ void expert_ffn(const void* x_rows, int act, int64_t M, int D, int I,
       g += xv * Wg[(size_t)(i * D + d)];
       u += xv * Wu[(size_t)(i * D + d)];
     }
-    double a = g / (1.0 + std::exp(-g)) * u;  // SiLU(g) * u
+    double a = glu_value(g, u, glu);
     double hv = (act == ACT_F32) ? (double)(float)a : (double)bf16_value(bf16_round(a));
     h[(size_t)ri] = hv;
     if (h_out) act_store(h_out, act, ri, hv);
@@ -268,6 +296,7 @@ extern "C" {
 
 /* ---- scalar numerics, exposed for the pins ------------------------------- */
 float orc_exp(float x) { return routing_exp(x); }
+double orc_glu_value(double g, double u, int glu) { return glu_value(g, u, glu); }
 float orc_sigmoid(float l) { return routing_sigmoid(l); }
 uint16_t orc_bf16_from_f64(double d) { return bf16_round(d); }
 uint16_t orc_bf16_from_f32(float f) { return bf16_round((double)f); }
@@ -334,15 +363,16 @@ int orc_permute(const int32_t* topk_idx, int64_t T, int k, int E, int32_t* count
 }
 
 /* ---- one expert's SwiGLU FFN over M rows (DS 6.5 SwiGLU; LD GLU branches) */
-/* wdtype: 0 fp32, 1 bf16, 2 mxfp4 (packed codes [.., cols/2] + scales [.., cols/32]). */
+/* wdtype: 0 fp32, 1 bf16, 2 mxfp4 (packed codes [.., cols/2] + scales [.., cols/32]).
+ * glu: gated activation (GLU_SWIGLU, GLU_CLAMP or GLU_SITU, see glu_value). */
 void orc_expert_ffn(const void* x_rows, int act, int64_t M, int D, int I, int wdtype,
                     const void* gate, const void* up, const void* down,
                     const uint8_t* gate_scale, const uint8_t* up_scale,
-                    const uint8_t* down_scale, void* out, void* h_out) {
+                    const uint8_t* down_scale, void* out, void* h_out, int glu) {
   std::vector<double> Wg = weight_matrix(gate, gate_scale, wdtype, I, D);
   std::vector<double> Wu = weight_matrix(up, up_scale, wdtype, I, D);
   std::vector<double> Wd = weight_matrix(down, down_scale, wdtype, D, I);
-  expert_ffn(x_rows, act, M, D, I, Wg, Wu, Wd, out, h_out, nullptr);
+  expert_ffn(x_rows, act, M, D, I, Wg, Wu, Wd, out, h_out, nullptr, glu);
 }
 
 /* ---- combine (FW trap 3 + case study: fp32 sum, one final cast) --------- */
@@ -373,7 +403,8 @@ void orc_combine(const void* expert_out, const int32_t* topk_idx, const float* t
 /* ---- the whole layer ------------------------------------------------------ */
 /* Weights are given per expert (pointer arrays of length E, NULL allowed for
  * experts no token selects).  macs[3] (optional) receives the multiply-adds
- * the oracle executed: router, routed experts, shared expert. */
+ * the oracle executed: router, routed experts, shared expert.  glu: the gated
+ * activation of every expert FFN of the layer (see glu_value). */
 typedef struct {
   int wdtype;
   const void* const* gate;
@@ -388,7 +419,7 @@ int orc_layer_forward(const void* x, int act, const int32_t* token_ids, const vo
                       const float* bias, const orc_experts* routed, const void* sh_gate,
                       const void* sh_up, const void* sh_down, int64_t T, int D, int E, int k,
                       int I, int I_shared, int mode, void* y, int32_t* topk_idx_out,
-                      float* topk_w_out, uint64_t* macs) {
+                      float* topk_w_out, uint64_t* macs, int glu) {
   if (k < 1 || k > E) return -2;
   const int64_t R = T * k;
   std::vector<float> logits;
@@ -428,7 +459,7 @@ int orc_layer_forward(const void* x, int act, const int32_t* token_ids, const vo
                                            routed->down_scale ? routed->down_scale[e] : nullptr,
                                            routed->wdtype, D, I);
     expert_ffn(xr.data(), act, M, D, I, Wg, Wu, Wd, &o[(size_t)offsets[e] * D * esz], nullptr,
-               &mac_routed);
+               &mac_routed, glu);
   }
   if (I_shared > 0) {
     s.resize((size_t)T * D * esz);
@@ -436,7 +467,7 @@ int orc_layer_forward(const void* x, int act, const int32_t* token_ids, const vo
     std::vector<double> Wg = weight_matrix(sh_gate, nullptr, sw, I_shared, D);
     std::vector<double> Wu = weight_matrix(sh_up, nullptr, sw, I_shared, D);
     std::vector<double> Wd = weight_matrix(sh_down, nullptr, sw, D, I_shared);
-    expert_ffn(x, act, T, D, I_shared, Wg, Wu, Wd, s.data(), nullptr, &mac_shared);
+    expert_ffn(x, act, T, D, I_shared, Wg, Wu, Wd, s.data(), nullptr, &mac_shared, glu);
   }
   orc_combine(o.data(), idx.data(), w.data(), pair_row.data(), I_shared > 0 ? s.data() : nullptr,
               T, k, D, act, y);
