@@ -41,6 +41,8 @@ def parse():
     p.add_argument("--config", type=int, default=2, help="layer recipe (1..5), default 2")
     p.add_argument("--T", type=int, default=None, help="override the batch size")
     p.add_argument("--replicas", type=int, default=0, help="weight replicas (0 = auto)")
+    p.add_argument("--glu", choices=("swiglu", "clamp", "situ"), default="swiglu",
+                   help="gated activation of the expert FFNs (clamped SwiGLU, SiTU-GLU)")
     p.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV",
                                                           "CAL_FETCH_CSV", "CAL_WRITE_CSV"),
                    help="turn rocprofv3 --pmc counter CSVs (FETCH_SIZE run, WRITE_SIZE run, and "
@@ -188,7 +190,7 @@ def main():
         wbytes_routed += 3 * dl.gate_scale.numel()
     # replicas so the weights do not stay in the 256 MB last-level cache
     nrep = args.replicas or max(1, min(8, int(np.ceil(1.2e9 / max(wbytes_routed, 1)))))
-    layers = [sdev.layer_object(dl)]
+    layers = [sdev.layer_object(dl, args.glu)]
     for _ in range(nrep - 1):
         c = sdev.DeviceLayer(cfg, dl.w_router, dl.bias, dl.gate.clone(), dl.up.clone(),
                              dl.down.clone(),
@@ -198,7 +200,7 @@ def main():
                              None if dl.sh_gate is None else dl.sh_gate.clone(),
                              None if dl.sh_up is None else dl.sh_up.clone(),
                              None if dl.sh_down is None else dl.sh_down.clone())
-        layers.append(sdev.layer_object(c))
+        layers.append(sdev.layer_object(c, args.glu))
     x = sdev.x_device(cfg, dev)
     ids = sdev.token_ids_device(cfg, dev)
     y = torch.empty((cfg.T, cfg.D), dtype=x.dtype, device=dev)
@@ -309,7 +311,7 @@ def main():
         while runs == 0 or t_cpu < args.cpu_seconds:
             c0 = time.perf_counter()
             oracle.layer_forward(xs, idsn, wr, bias, experts, sh, T_s, D, E, k, I,
-                                 Is, cfg.route, cfg.wdtype)
+                                 Is, cfg.route, cfg.wdtype, glu=args.glu)
             t_cpu += time.perf_counter() - c0
             runs += 1
         cpu = {"value": round(runs * T_s / t_cpu, 2), "unit": "tokens/s",
@@ -333,9 +335,11 @@ def main():
         "data": "synthetic (seeded Philox inputs of the recipe's shapes and distributions)",
         "config": {"workload": f"MoE layer recipe {cfg.cid} ({cfg.name}): T={T}, D={D}, E={E} "
                                f"routed + {1 if Is else 0} shared, top-{k} {cfg.route}, I={I}, "
-                               f"I_shared={Is}, weights {cfg.wdtype}",
+                               f"I_shared={Is}, weights {cfg.wdtype}"
+                               + ("" if args.glu == "swiglu" else f", {args.glu} activation"),
                    "T": T, "D": D, "E": E, "k": k, "I": I, "I_shared": Is,
-                   "routing": cfg.route, "weights": cfg.wdtype, "parallelism": "single GPU",
+                   "routing": cfg.route, "weights": cfg.wdtype, "activation": args.glu,
+                   "parallelism": "single GPU",
                    "weight_replicas": nrep, "experts_touched": U,
                    "max_rows_per_expert": int(counts.max())},
         "roofline": roofline,

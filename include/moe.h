@@ -63,9 +63,22 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOPK 32
+
+/* flags of moe_grouped_swiglu and moe_layer_forward: the gated activation of
+ * every expert FFN the call runs (routed and shared experts alike).  0 is
+ * SwiGLU, SiLU(g) * u with g = W_g x, u = W_u x.  At most one of:
+ *   MOE_FLAG_GLU_CLAMP  the clamped SwiGLU of [DS] 6.5: g is capped from above
+ *                       at 10 and u clamped to [-10, 10], then SiLU(g) * u;
+ *   MOE_FLAG_GLU_SITU   SiTU-GLU ([LD], section SiTU-GLU):
+ *                       [4 tanh(g / 4) * sigmoid(g)] * [25 tanh(u / 25)].
+ * Both act on the fp32 GEMM results before the one rounding of h, per element
+ * and the same for every T, so the determinism contract below is unchanged.
+ * Both bits together, or any other bit, give MOE_ERR_UNSUPPORTED. */
+#define MOE_FLAG_GLU_CLAMP 0x1u
+#define MOE_FLAG_GLU_SITU 0x2u
 
 typedef enum {
   MOE_OK = 0,
@@ -167,6 +180,7 @@ int moe_permute(const int32_t* topk_idx, int64_t T, int k, int E, int32_t* exper
  * for every row r of expert e (expert_offsets[e] <= r < expert_offsets[e+1]),
  *   g = W_gate[e] a_r, u = W_up[e] a_r        (fp32 accumulation, full K = D)
  *   h = round(silu(g) * u),  silu(g) = g / (1 + e^-g)
+ *       (or the activation that flags select: MOE_FLAG_GLU_CLAMP / _SITU)
  *   out[r] = round(W_down[e] h)               (fp32 accumulation, full K = I)
  * where a_r = x_rows[row_index[r]] if row_index is not NULL, else x_rows[r],
  * and round() is bf16 round-to-nearest-even (bf16/MXFP4 weights) or the fp32
@@ -175,7 +189,7 @@ int moe_permute(const int32_t* topk_idx, int64_t T, int k, int E, int32_t* exper
  * Rows of one expert never interact: each row's output is independent of the
  * other rows and of their number.
  *  R: number of rows (= expert_offsets[E]); for a shared expert pass E = 1 and
- *  expert_offsets = {0, T}.  flags: must be 0 (reserved).
+ *  expert_offsets = {0, T}.  flags: 0, MOE_FLAG_GLU_CLAMP or MOE_FLAG_GLU_SITU.
  *  row_index entries must be valid rows of x_rows (they are not checked).
  *  workspace: moe_grouped_swiglu_workspace_bytes(R, E, D, I, act) bytes
  *  (h rows, and the tile tables that the call writes from expert_offsets).
@@ -204,7 +218,8 @@ int moe_combine(const void* expert_out, const int32_t* topk_idx, const float* to
  * The residual connection is not part of the layer.
  *  routed: E experts; shared: NULL (no shared expert, I_shared ignored) or one
  *  expert with inter dim I_shared (bf16 when routed weights are MXFP4).
- *  flags: must be 0 (reserved for per-fusion variants).
+ *  flags: 0, MOE_FLAG_GLU_CLAMP or MOE_FLAG_GLU_SITU (the gated activation of
+ *  the routed and the shared experts).
  *  workspace: moe_layer_workspace_bytes(...) bytes.
  * ------------------------------------------------------------------------- */
 size_t moe_layer_workspace_bytes(int64_t T, int D, int E, int k, int I, int I_shared,

@@ -19,6 +19,8 @@ LIB_PATH = os.path.join(_HERE, "libinvariant_moe.so")
 
 F32, BF16, MXFP4 = 0, 1, 2
 ROUTE = {"softmax": 0, "sigmoid": 1, "hash": 2}
+# flags values selecting the gated activation (MOE_FLAG_GLU_* in moe.h)
+GLU = {"swiglu": 0, "clamp": 0x1, "situ": 0x2}
 STAGES = ("routing", "permute", "gate_up_gemm", "down_gemm", "combine")
 EXPORTS = ("moe_router_workspace_bytes", "moe_router_topk", "moe_routing_scores", "moe_permute_workspace_bytes",
            "moe_permute", "moe_grouped_swiglu_workspace_bytes", "moe_grouped_swiglu",
@@ -184,8 +186,8 @@ def permute(topk_idx, E: int, x=None, stream=None):
 
 
 def grouped_swiglu(x_rows, row_index, expert_offsets, R: int, E: int, weights: ExpertWeights,
-                   out=None, stream=None):
-    """Expert FFN over grouped rows: out [R, D]."""
+                   out=None, stream=None, glu: str = "swiglu"):
+    """Expert FFN over grouped rows: out [R, D].  glu: "swiglu", "clamp" or "situ"."""
     D = x_rows.shape[1]
     I = weights.gate.shape[1]
     act = _act(x_rows)
@@ -196,7 +198,7 @@ def grouped_swiglu(x_rows, row_index, expert_offsets, R: int, E: int, weights: E
     ws = _workspace(nb, x_rows.device)
     wst = weights.as_struct()
     _check(L.moe_grouped_swiglu(_ptr(x_rows), _ptr(row_index), _ptr(expert_offsets), R, E, D, I,
-                                ctypes.byref(wst), act, 0, _ptr(out), _ptr(ws), nb,
+                                ctypes.byref(wst), act, GLU[glu], _ptr(out), _ptr(ws), nb,
                                 _stream(stream)))
     return out
 
@@ -219,8 +221,8 @@ def layer_workspace_bytes(T, D, E, k, I, I_shared, act, wdtype) -> int:
 
 def layer_forward(x, token_ids, w_router, bias, routed: ExpertWeights,
                   shared: Optional[ExpertWeights], E: int, k: int, mode: str, out=None,
-                  workspace=None, stream=None):
-    """The whole layer: y [T, D]."""
+                  workspace=None, stream=None, glu: str = "swiglu"):
+    """The whole layer: y [T, D].  glu: the gated activation of every expert FFN."""
     T, D = x.shape
     I = routed.gate.shape[1]
     Is = shared.gate.shape[1] if shared is not None else 0
@@ -237,7 +239,7 @@ def layer_forward(x, token_ids, w_router, bias, routed: ExpertWeights,
     s = shared.as_struct() if shared is not None else None
     _check(L.moe_layer_forward(_ptr(x), _ptr(token_ids), _ptr(w_router), _ptr(bias),
                                ctypes.byref(r), ctypes.byref(s) if s is not None else None,
-                               T, D, E, k, I, Is, ROUTE[mode], act, 0, _ptr(out), ws_ptr,
+                               T, D, E, k, I, Is, ROUTE[mode], act, GLU[glu], _ptr(out), ws_ptr,
                                ws_bytes, _stream(stream)))
     return out
 
@@ -258,9 +260,9 @@ class MoELayer:
     """Device-resident layer weights plus a reusable workspace."""
 
     def __init__(self, w_router, bias, routed: ExpertWeights, shared: Optional[ExpertWeights],
-                 E: int, k: int, mode: str):
+                 E: int, k: int, mode: str, glu: str = "swiglu"):
         self.w_router, self.bias, self.routed, self.shared = w_router, bias, routed, shared
-        self.E, self.k, self.mode = E, k, mode
+        self.E, self.k, self.mode, self.glu = E, k, mode, glu
         self._ws = None
 
     def forward(self, x, token_ids=None, out=None, stream=None):
@@ -272,4 +274,4 @@ class MoELayer:
             self._ws = _workspace(nb, x.device)
         return layer_forward(x, token_ids, self.w_router, self.bias, self.routed, self.shared,
                              self.E, self.k, self.mode, out=out, workspace=self._ws,
-                             stream=stream)
+                             stream=stream, glu=self.glu)

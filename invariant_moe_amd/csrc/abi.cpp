@@ -29,6 +29,18 @@ int ok() {
   return MOE_OK;
 }
 
+// The gated activation that a call's flags select (MOE_FLAG_GLU_*).
+int glu_from_flags(uint32_t flags, int* glu) {
+  constexpr uint32_t known = MOE_FLAG_GLU_CLAMP | MOE_FLAG_GLU_SITU;
+  if (flags & ~known) return fail(MOE_ERR_UNSUPPORTED, "flags 0x%x: unknown bits", flags);
+  if (flags == known)
+    return fail(MOE_ERR_UNSUPPORTED, "flags 0x%x: at most one gated activation", flags);
+  *glu = (flags & MOE_FLAG_GLU_CLAMP) ? moe::GLU_CLAMP
+         : (flags & MOE_FLAG_GLU_SITU) ? moe::GLU_SITU
+                                       : moe::GLU_SWIGLU;
+  return MOE_OK;
+}
+
 int hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return ok();
   return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -320,7 +332,8 @@ int moe_grouped_swiglu(const void* x_rows, const int32_t* row_index, const int32
                        void* stream) {
   int rc;
   if ((rc = check_act(act))) return rc;
-  if (flags) return fail(MOE_ERR_UNSUPPORTED, "flags 0x%x not supported", flags);
+  int glu;
+  if ((rc = glu_from_flags(flags, &glu))) return rc;
   if (R < 0 || R >= ((int64_t)1 << 31)) return fail(MOE_ERR_SHAPE, "R out of range");
   if (E < 1 || E > MOE_MAX_EXPERTS) return fail(MOE_ERR_SHAPE, "E=%d out of range", E);
   if (D < 32 || D % 32 || I < 32 || I % 32)
@@ -350,6 +363,7 @@ int moe_grouped_swiglu(const void* x_rows, const int32_t* row_index, const int32
   moe::GemmArgs up{};
   up.nseg = 1;
   up.seg[0] = make_seg(x_rows, row_index, expert_offsets, R, E, D, I, w, true, workspace);
+  up.glu = glu;
   if (e == hipSuccess) e = moe::launch_grouped_gemm(p.up, up, tiles_up, s);
   if (e == hipSuccess) {
     moe::GemmArgs dn{};
@@ -393,7 +407,8 @@ int moe_layer_forward(const void* x, const int32_t* token_ids, const void* w_rou
   int rc;
   if ((rc = check_act(act))) return rc;
   if ((rc = check_dims(T, D, E, k))) return rc;
-  if (flags) return fail(MOE_ERR_UNSUPPORTED, "flags 0x%x not supported", flags);
+  int glu;
+  if ((rc = glu_from_flags(flags, &glu))) return rc;
   if (I < 32 || I % 32) return fail(MOE_ERR_SHAPE, "I=%d must be a positive multiple of 32", I);
   if (mode != MOE_ROUTE_SOFTMAX && mode != MOE_ROUTE_SIGMOID && mode != MOE_ROUTE_HASH)
     return fail(MOE_ERR_SHAPE, "unknown routing mode %d", (int)mode);
@@ -465,6 +480,7 @@ int moe_layer_forward(const void* x, const int32_t* token_ids, const void* w_rou
   moe::GemmArgs up{};
   up.seg[0] = make_seg(x, row_token, offsets, R, E, D, I, routed, true, h);
   up.nseg = 1;
+  up.glu = glu;
   if (shared) {
     up.seg[1] = make_seg(x, nullptr, nullptr, T, 1, D, Is, shared, true, hs);
     up.nseg = 2;

@@ -78,9 +78,52 @@ __device__ __forceinline__ bool read_tile(const GemmArgs& a, int BM, TileInfo& t
   return true;
 }
 
-__device__ __forceinline__ float silu_mul(float g, float u) {
-  return g / (1.0f + __expf(-g)) * u;
+// The gated activation a(g, u) of the gate branch g and the up branch u, in
+// fp32 (M: the math of the kernel, FastMath or LibMath below):
+//  GLU_SWIGLU  SiLU(g) * u;
+//  GLU_CLAMP   the clamped SwiGLU of the DeepSeek-V4 infrastructure
+//              walkthrough, section 6.5: g capped from above at 10, u clamped
+//              to [-10, 10], then SiLU(g) * u;
+//  GLU_SITU    SiTU-GLU (forum article on MoE variants, section "SiTU-GLU"):
+//              the soft cap b tanh(x / b) on each branch, b = 4 on the gate and
+//              25 on the up branch, times the sigmoid of the uncapped gate.
+// The comparisons keep a NaN branch value NaN.  Per element and uniform over
+// the launch, so the activation never depends on the batch.
+template <typename M>
+__device__ __forceinline__ float glu_act(float g, float u, int glu) {
+  if (glu == GLU_SITU)
+    return M::softcap(g, 4.0f, 0.25f) * M::recip(1.0f + M::exp(-g)) *
+           M::softcap(u, 25.0f, 0.04f);
+  if (glu == GLU_CLAMP) {
+    g = g > 10.0f ? 10.0f : g;
+    u = u > 10.0f ? 10.0f : (u < -10.0f ? -10.0f : u);
+  }
+  return g / (1.0f + M::exp(-g)) * u;
 }
+
+// bf16 outputs (8 significant bits): hardware exp and reciprocal, and tanh
+// from one exponential, tanh|x| = (1 - e) / (1 + e) with e = exp(-2|x|), or,
+// below |x| = 1/16 where 1 - e cancels, the odd Taylor terms
+// x - x^3/3 + 2x^5/15 (truncation under 4e-9 relative there).
+struct FastMath {
+  static __device__ float exp(float a) { return __expf(a); }
+  static __device__ float recip(float a) { return __builtin_amdgcn_rcpf(a); }
+  static __device__ float tanh(float x) {
+    const float ax = fabsf(x), x2 = x * x;
+    const float e = __expf(-2.0f * ax);
+    const float big = (1.0f - e) * __builtin_amdgcn_rcpf(1.0f + e);
+    const float small = ax * (1.0f + x2 * (-1.0f / 3.0f + x2 * (2.0f / 15.0f)));
+    return copysignf(ax < 0.0625f ? small : big, x);
+  }
+  static __device__ float softcap(float x, float b, float inv_b) { return b * tanh(x * inv_b); }
+};
+
+// fp32 outputs: the device library's functions and IEEE division.
+struct LibMath {
+  static __device__ float exp(float a) { return expf(a); }
+  static __device__ float recip(float a) { return 1.0f / a; }
+  static __device__ float softcap(float x, float b, float) { return b * tanhf(x / b); }
+};
 
 // Exact decode of 32 E2M1 codes (16 bytes, element 2i in the low nibble of
 // byte i) with one E8M0 scale byte into 32 bf16 values, by gfx950's scaled
@@ -433,7 +476,8 @@ __global__ __launch_bounds__(64 * WM * WN, 2) void k_grouped_gemm_bf16(GemmArgs 
         float v[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          v[i] = GATED ? silu_mul(acc[0][nb][tb][i], acc[NMAT - 1][nb][tb][i]) : acc[0][nb][tb][i];
+          v[i] = GATED ? glu_act<FastMath>(acc[0][nb][tb][i], acc[NMAT - 1][nb][tb][i], args.glu)
+                       : acc[0][nb][tb][i];
         uint2 pk = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
         *reinterpret_cast<uint2*>(out + (ti.row0 + r) * (int64_t)N + n) = pk;
       }
@@ -479,7 +523,7 @@ __global__ __launch_bounds__(256) void k_grouped_gemm_f32(GemmArgs args) {
       for (int m = 0; m < NMAT; ++m) acc[m] = __builtin_fmaf(As[r][kk], Bs[m][n][kk], acc[m]);
   }
   if (r < ti.rows && ti.n0 + n < N) {
-    const float v = GATED ? acc[0] / (1.0f + expf(-acc[0])) * acc[NMAT - 1] : acc[0];
+    const float v = GATED ? glu_act<LibMath>(acc[0], acc[NMAT - 1], args.glu) : acc[0];
     static_cast<float*>(s.out)[(ti.row0 + r) * (int64_t)N + ti.n0 + n] = v;
   }
 }
@@ -666,6 +710,7 @@ hipError_t launch_grouped_gemm(const GemmPlan& p, const GemmArgs& a, int4* table
     for (int sg = 0; sg < a.nseg; ++sg)
       if (L.seg_mask & (1 << sg)) one.seg[one.nseg++] = a.seg[sg];
     one.tiles = tables;
+    one.glu = a.glu;
     const LaunchEvents ev{i == 0 ? ev_start : nullptr, i == p.n - 1 ? ev_stop : nullptr};
     hipError_t e;
     if (L.cfg == TILE_F32) {

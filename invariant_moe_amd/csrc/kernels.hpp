@@ -32,7 +32,11 @@ struct GemmArgs {
   GemmSeg seg[2];
   int nseg;
   const int4* tiles;  // [grid] descriptors, indexed by blockIdx.x
+  int glu;            // gated activation of a gated GEMM (GluMode)
 };
+
+// Gated activation of the gate/up GEMM's epilogue.
+enum GluMode { GLU_SWIGLU = 0, GLU_CLAMP = 1, GLU_SITU = 2 };
 
 // Shape of a segment as the host planner sees it.
 struct SegShape {

@@ -3,6 +3,8 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
+
 requires_gpu = pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")
 
 
@@ -43,3 +45,19 @@ def dev(a: np.ndarray, device="cuda") -> torch.Tensor:
 
 def banner(msg: str) -> None:
     print(f"[gpu-test] {msg}", flush=True)
+
+
+def mxfp4_decode_bf16(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Oracle decode of MXFP4 codes/scales [G, rows, cols/2], [G, rows, cols/32] to
+    bf16 bit patterns [G, rows, cols]."""
+    G, rows, half = packed.shape
+    lo, hi = packed & 0xF, packed >> 4
+    codes = np.stack([lo, hi], -1).reshape(G, rows, half * 2)
+    sc = np.repeat(scales, 32, axis=-1)
+    table = np.array([[oracle.lib().orc_mxfp4_value(c, s) for s in range(256)] for c in range(16)])
+    return oracle.bf16_from_f64_array(table[codes, sc])
+
+
+def mxfp4_pack(codes: np.ndarray) -> np.ndarray:
+    """E2M1 codes [..., cols] -> bytes [..., cols/2], element 2i in the low nibble."""
+    return (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)

@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert set(moe.EXPORTS) <= set(names)
-    assert L.moe_abi_version() == 2
+    assert L.moe_abi_version() == 3
 
 
 def test_status_strings():
@@ -84,7 +84,9 @@ def _layer(**kw):
     (dict(x=_fake(0x100008)), -4),             # misaligned
     (dict(wsb=16), -5),
     (dict(ws=None), -5),
-    (dict(flags=1), -6),
+    (dict(flags=3), -6),         # both gated activations
+    (dict(flags=4), -6),         # unknown flag bit
+    (dict(flags=0x80000001), -6),
     (dict(mode=2), -1),          # hash without token ids
     (dict(mode=7), -2),
     (dict(shared=_weights(), Is=40), -2),
@@ -96,8 +98,9 @@ def test_layer_forward_rejects(kw, status):
 
 
 def test_t_zero_is_a_noop_without_gpu_work():
-    rc, msg = _layer(T=0)
-    assert rc == 0 and msg == ""
+    for flags in (0, 1, 2):  # every accepted gated activation
+        rc, msg = _layer(T=0, flags=flags)
+        assert rc == 0 and msg == ""
 
 
 def test_workspace_query():
@@ -114,8 +117,9 @@ def test_workspace_query():
 def test_other_entry_points_reject():
     L = moe.lib()
     w = _weights()
-    assert L.moe_grouped_swiglu(_fake(), None, _fake(), 10, 4, 64, 64, ctypes.byref(w), 1, 1,
-                                _fake(), _fake(), 1 << 20, None) == -6  # flags
+    for flags in (3, 4, 0x100):  # two activations / unknown bits
+        assert L.moe_grouped_swiglu(_fake(), None, _fake(), 10, 4, 64, 64, ctypes.byref(w), 1,
+                                    flags, _fake(), _fake(), 1 << 20, None) == -6
     assert L.moe_grouped_swiglu(_fake(), None, _fake(), 10, 4, 64, 40, ctypes.byref(w), 1, 0,
                                 _fake(), _fake(), 1 << 20, None) == -2
     assert L.moe_combine(_fake(), _fake(), _fake(), _fake(), None, 4, 0, 64, 1, _fake(), None) == -2

@@ -14,6 +14,7 @@ import invariant_moe_amd as moe
 import oracle
 import synth
 from gpu_util import banner, dev, rel_l2, requires_gpu, to_np, tol_for
+from gpu_util import mxfp4_decode_bf16 as _decode_bf16, mxfp4_pack as _pack
 from synth import device as sdev
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
@@ -200,21 +201,6 @@ def test_determinism_repeat_and_streams():
         c = layer.forward(x, stream=s)
     s.synchronize()
     assert np.array_equal(a, b) and np.array_equal(a, to_np(c))
-
-
-def _decode_bf16(packed, scales):
-    """Oracle decode of MXFP4 codes/scales [G, rows, cols/2], [G, rows, cols/32] to
-    bf16 bit patterns [G, rows, cols]."""
-    G, rows, half = packed.shape
-    lo, hi = packed & 0xF, packed >> 4
-    codes = np.stack([lo, hi], -1).reshape(G, rows, half * 2)
-    sc = np.repeat(scales, 32, axis=-1)
-    table = np.array([[oracle.lib().orc_mxfp4_value(c, s) for s in range(256)] for c in range(16)])
-    return oracle.bf16_from_f64_array(table[codes, sc])
-
-
-def _pack(codes):
-    return (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
 
 
 def test_mxfp4_equals_bf16_on_decoded_weights():
