@@ -60,6 +60,7 @@ def lib():
         L.orc_expert_ffn.argtypes = [vp, i32, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp,
                                      i32]
         L.orc_combine.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i32, vp]
+        L.orc_residual_rmsnorm.argtypes = [vp, vp, vp, ctypes.c_double, i64, i32, i32, vp, vp]
         L.orc_layer_forward.argtypes = [vp, i32, vp, vp, vp, ctypes.POINTER(_Experts), vp, vp, vp,
                                         i64, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, i32]
         L.orc_layer_forward.restype = i32
@@ -169,6 +170,25 @@ def combine(expert_out, topk_idx, topk_w, pair_row, shared_out, T, k, D):
     lib().orc_combine(_p(expert_out), _p(topk_idx), _p(topk_w), _p(pair_row), _p(shared_out),
                       T, k, D, ACT[act_name(expert_out)], _p(y))
     return y
+
+
+def residual_rmsnorm(x, residual, gamma, eps: float):
+    """h = round(x + residual), normed = round(g * h / sqrt(mean(h^2) + eps)) per row.
+    Returns (residual_out, normed), both of x's dtype (see orc_residual_rmsnorm)."""
+    T, D = x.shape
+    assert residual.shape == x.shape and gamma.shape == (D,) and residual.dtype == x.dtype
+    res_out = np.empty_like(x)
+    normed = np.empty_like(x)
+    lib().orc_residual_rmsnorm(_p(x), _p(residual), _p(gamma), eps, T, D, ACT[act_name(x)],
+                               _p(res_out), _p(normed))
+    return res_out, normed
+
+
+def combine_rmsnorm(expert_out, topk_idx, topk_w, pair_row, shared_out, residual, gamma, eps,
+                    T, k, D):
+    """The unfused MoE tail: combine, then the residual add and RMSNorm of its output."""
+    y = combine(expert_out, topk_idx, topk_w, pair_row, shared_out, T, k, D)
+    return residual_rmsnorm(y, residual, gamma, eps)
 
 
 def layer_forward(x, token_ids, w_router, bias, experts: dict, shared, T, D, E, k, I,

@@ -400,6 +400,37 @@ void orc_combine(const void* expert_out, const int32_t* topk_idx, const float* t
   }
 }
 
+/* ---- residual add + RMSNorm (the next block's input norm) ---------------- */
+/* The unfused MoE tail of [FW] trap 3 ends with rmsnorm(full_out + residual);
+ * RMSNorm itself as in [LD] "RMSNorm before up-projection":
+ *   RMSNorm(h) = g * h / sqrt(mean_d(h^2) + eps).
+ * Readings (this library's definition): the residual stream is kept in the
+ * activation type, so h = round(x + residual) is rounded before the norm sees
+ * it (as the unfused kernels write it to memory), and the normalised value is
+ * rounded once.  Everything between the two roundings is in double here.
+ *   residual_out[t] = h[t] = round(x[t] + residual[t])
+ *   normed[t, d] = round(g[d] * h[t, d] / sqrt(sum_d h[t, d]^2 / D + eps))
+ * x, residual, gamma, residual_out, normed in the activation type. */
+void orc_residual_rmsnorm(const void* x, const void* residual, const void* gamma, double eps,
+                          int64_t T, int D, int act, void* residual_out, void* normed) {
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    std::vector<double> h((size_t)D);
+    double ss = 0.0;
+    for (int d = 0; d < D; ++d) {
+      const int64_t i = t * D + d;
+      const double sum = act_at(x, act, i) + act_at(residual, act, i);
+      h[(size_t)d] = (act == ACT_F32) ? (double)(float)sum : (double)bf16_value(bf16_round(sum));
+      ss += h[(size_t)d] * h[(size_t)d];
+    }
+    const double rms = std::sqrt(ss / D + eps);
+    for (int d = 0; d < D; ++d) {
+      act_store(residual_out, act, t * D + d, h[(size_t)d]);
+      act_store(normed, act, t * D + d, act_at(gamma, act, d) * h[(size_t)d] / rms);
+    }
+  }
+}
+
 /* ---- the whole layer ------------------------------------------------------ */
 /* Weights are given per expert (pointer arrays of length E, NULL allowed for
  * experts no token selects).  macs[3] (optional) receives the multiply-adds
