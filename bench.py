@@ -154,6 +154,66 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
 
 
+def tail_measurement(cfg, hip, sptr, steps: int):
+    """The MoE tail at the recipe's shape: the combine fused with the next
+    block's residual add + RMSNorm (one kernel), against the combine followed
+    by the standalone norm (two kernels, y written and read back).  Synthetic
+    expert outputs, shared output, residual and gain; distinct random experts
+    per token and a random pair -> row permutation."""
+    import torch
+
+    import invariant_moe_amd as moe
+
+    T, D, E, k = cfg.T, cfg.D, cfg.E, cfg.k
+    R = T * k
+    dt = torch.float32 if cfg.act == "f32" else torch.bfloat16
+    es = 4 if cfg.act == "f32" else 2
+    g = torch.Generator(device="cuda").manual_seed(1234)
+    o = torch.randn((R, D), device="cuda", generator=g).to(dt)
+    sh = torch.randn((T, D), device="cuda", generator=g).to(dt) if cfg.I_shared else None
+    res = torch.randn((T, D), device="cuda", generator=g).to(dt)
+    gamma = (1.0 + 0.1 * torch.randn(D, device="cuda", generator=g)).to(dt)
+    idx = torch.rand((T, E), device="cuda", generator=g).argsort(dim=1)[:, :k].to(torch.int32)
+    w = torch.rand((T, k), device="cuda", generator=g)
+    w = (w / w.sum(1, keepdim=True)).contiguous()
+    pair_row = torch.randperm(R, device="cuda", generator=g).to(torch.int32)
+    idx = idx.contiguous()
+    y = torch.empty((T, D), dtype=dt, device="cuda")
+    h = torch.empty_like(res)
+    n = torch.empty_like(res)
+    eps = 1e-6
+
+    def unfused():
+        moe.combine(o, idx, w, pair_row, sh, out=y)
+        moe.residual_rmsnorm(y, res, gamma, eps, residual_out=h, normed=n)
+
+    def fused():
+        moe.combine_rmsnorm(o, idx, w, pair_row, sh, res, gamma, eps, residual_out=h, normed=n)
+
+    out = {}
+    for name, fn in (("unfused", unfused), ("fused", fused)):
+        for _ in range(3):
+            fn()
+        a, b = hip.event(), hip.event()
+        torch.cuda.synchronize()
+        hip.record(a, sptr)
+        for _ in range(steps):
+            fn()
+        hip.record(b, sptr)
+        torch.cuda.synchronize()
+        out[name] = hip.elapsed_ms(a, b) / steps
+    # algorithmic bytes of the fused kernel: expert rows, shared row, residual
+    # in, residual and normed out, gain, slot indices / weights / rows
+    fused_bytes = (R * D + (T * D if sh is not None else 0) + 3 * T * D + D) * es + R * 12
+    unfused_bytes = fused_bytes + 2 * T * D * es  # y written, then read
+    gbs = fused_bytes / (out["fused"] * 1e-3) / 1e9
+    return {"fused_us": round(out["fused"] * 1e3, 2), "unfused_us": round(out["unfused"] * 1e3, 2),
+            "fused_alg_bytes": int(fused_bytes), "unfused_alg_bytes": int(unfused_bytes),
+            "fused_gbs": round(gbs, 1), "fused_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "unfused_gbs": round(unfused_bytes / (out["unfused"] * 1e-3) / 1e9, 1),
+            "kernel": "k_residual_rmsnorm (combine fused with residual add + RMSNorm)"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -256,6 +316,8 @@ def main():
         kern_ms = stage_avg[[2, 3]]
     gu_ms = float(kern_ms[0])
 
+    tail = tail_measurement(cfg, hip, sptr, min(K, 50))
+
     # algorithmic work of the gate/up SwiGLU GEMM launch (routed + shared groups)
     T, D, E, k, I, Is = cfg.T, cfg.D, cfg.E, cfg.k, cfg.I, cfg.I_shared
     R = T * k
@@ -344,6 +406,7 @@ def main():
                    "max_rows_per_expert": int(counts.max())},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "tail": tail,
         "layer": {"alg_bytes": int(layer_bytes), "flops": int(layer_flops),
                   "gbs": round(layer_bytes / (ms_per_step * 1e-3) / 1e9, 1),
                   "hbm_frac": round(layer_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

@@ -213,6 +213,42 @@ int moe_combine(const void* expert_out, const int32_t* topk_idx, const float* to
                 moe_dtype act, void* y, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * moe_residual_rmsnorm — the residual add and RMSNorm of the next block's
+ * input, the last kernel of the unfused MoE tail ([FW] trap 3:
+ * rmsnorm(out + residual)); RMSNorm as [LD] defines it (section "RMSNorm
+ * before up-projection"), g * h / sqrt(mean(h^2) + eps):
+ *   h[t] = round(x[t] + residual[t])                  -> residual_out[t]
+ *   ss = sum over d of h[t,d]^2                        (fp32, order below)
+ *   normed[t,d] = round(gamma[d] * (h[t,d] * (1 / sqrt(ss / D + eps))))
+ * round() is bf16 RNE (bf16) or the fp32 value itself; the norm sees the
+ * rounded residual.  Order of ss, the same for every T and for both entry
+ * points ([FW] trap 2: the norm's reduction tree must not follow the launch
+ * layout): 1024 partials, partial p sums h[d]^2 with fmaf from +0 over the
+ * 8-feature chunks c = d/8 with c % 1024 == p, in increasing d; then
+ * p += p + m for m = 512, 256, ..., 1; the division, square root and
+ * reciprocal are IEEE fp32.
+ *  x, residual, residual_out, normed [T, D]; gamma [D]; all act dtype.
+ *  residual_out may be residual itself (in place); no other overlap.
+ *  D: a positive multiple of 32.  eps: finite and >= 0 (else
+ *  MOE_ERR_UNSUPPORTED).
+ * ------------------------------------------------------------------------- */
+int moe_residual_rmsnorm(const void* x, const void* residual, const void* gamma, float eps,
+                         int64_t T, int D, moe_dtype act, void* residual_out, void* normed,
+                         void* stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_combine_rmsnorm — moe_combine fused with moe_residual_rmsnorm of its
+ * output (the finalize + next-RMSNorm fusion of [FW] trap 3, without the
+ * all-reduce): the bits of moe_combine into y followed by
+ * moe_residual_rmsnorm(y, residual, ...), without writing or reading y.
+ * Arguments as in those two calls.
+ * ------------------------------------------------------------------------- */
+int moe_combine_rmsnorm(const void* expert_out, const int32_t* topk_idx, const float* topk_w,
+                        const int32_t* pair_row, const void* shared_out, const void* residual,
+                        const void* gamma, float eps, int64_t T, int k, int D, moe_dtype act,
+                        void* residual_out, void* normed, void* stream);
+
+/* ---------------------------------------------------------------------------
  * moe_layer_forward — the whole layer: route, permute, grouped SwiGLU over the
  * routed rows and the shared expert (one launch for both), combine.  y [T, D].
  * The residual connection is not part of the layer.

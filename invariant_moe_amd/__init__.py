@@ -24,7 +24,8 @@ GLU = {"swiglu": 0, "clamp": 0x1, "situ": 0x2}
 STAGES = ("routing", "permute", "gate_up_gemm", "down_gemm", "combine")
 EXPORTS = ("moe_router_workspace_bytes", "moe_router_topk", "moe_routing_scores", "moe_permute_workspace_bytes",
            "moe_permute", "moe_grouped_swiglu_workspace_bytes", "moe_grouped_swiglu",
-           "moe_combine", "moe_layer_workspace_bytes", "moe_layer_forward",
+           "moe_combine", "moe_residual_rmsnorm", "moe_combine_rmsnorm",
+           "moe_layer_workspace_bytes", "moe_layer_forward",
            "moe_set_stage_events", "moe_status_string", "moe_last_error", "moe_abi_version")
 
 
@@ -62,6 +63,10 @@ def lib() -> ctypes.CDLL:
         L.moe_grouped_swiglu_workspace_bytes.restype = sz
         L.moe_grouped_swiglu.argtypes = [vp, vp, vp, i64, i32, i32, i32, WP, i32, u32, vp, vp, sz, vp]
         L.moe_combine.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i32, vp, vp]
+        f32 = ctypes.c_float
+        L.moe_residual_rmsnorm.argtypes = [vp, vp, vp, f32, i64, i32, i32, vp, vp, vp]
+        L.moe_combine_rmsnorm.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32, i64, i32, i32, i32, vp,
+                                          vp, vp]
         L.moe_layer_workspace_bytes.argtypes = [i64, i32, i32, i32, i32, i32, i32, i32]
         L.moe_layer_workspace_bytes.restype = sz
         L.moe_layer_forward.argtypes = [vp, vp, vp, vp, WP, WP, i64, i32, i32, i32, i32, i32, i32,
@@ -71,7 +76,8 @@ def lib() -> ctypes.CDLL:
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_last_error.restype = ctypes.c_char_p
         for name in ("moe_router_topk", "moe_routing_scores", "moe_permute", "moe_grouped_swiglu", "moe_combine",
-                     "moe_layer_forward", "moe_set_stage_events", "moe_abi_version"):
+                     "moe_residual_rmsnorm", "moe_combine_rmsnorm", "moe_layer_forward",
+                     "moe_set_stage_events", "moe_abi_version"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -213,6 +219,37 @@ def combine(expert_out, topk_idx, topk_w, pair_row, shared_out, out=None, stream
                              _ptr(shared_out), T, k, D, _act(expert_out), _ptr(out),
                              _stream(stream)))
     return out
+
+
+def residual_rmsnorm(x, residual, gamma, eps: float, residual_out=None, normed=None,
+                     stream=None):
+    """h = round(x + residual) -> residual_out, RMSNorm(h) * gamma -> normed.
+    residual_out may be residual (in place).  Returns (residual_out, normed)."""
+    T, D = x.shape
+    if residual_out is None:
+        residual_out = torch.empty_like(x)
+    if normed is None:
+        normed = torch.empty_like(x)
+    _check(lib().moe_residual_rmsnorm(_ptr(x), _ptr(residual), _ptr(gamma), eps, T, D, _act(x),
+                                      _ptr(residual_out), _ptr(normed), _stream(stream)))
+    return residual_out, normed
+
+
+def combine_rmsnorm(expert_out, topk_idx, topk_w, pair_row, shared_out, residual, gamma,
+                    eps: float, residual_out=None, normed=None, stream=None):
+    """The combine fused with residual_rmsnorm of its output (same bits as the two
+    calls).  Returns (residual_out, normed)."""
+    T, k = topk_idx.shape
+    D = expert_out.shape[1]
+    if residual_out is None:
+        residual_out = torch.empty_like(residual)
+    if normed is None:
+        normed = torch.empty_like(residual)
+    _check(lib().moe_combine_rmsnorm(_ptr(expert_out), _ptr(topk_idx), _ptr(topk_w),
+                                     _ptr(pair_row), _ptr(shared_out), _ptr(residual),
+                                     _ptr(gamma), eps, T, k, D, _act(expert_out),
+                                     _ptr(residual_out), _ptr(normed), _stream(stream)))
+    return residual_out, normed
 
 
 def layer_workspace_bytes(T, D, E, k, I, I_shared, act, wdtype) -> int:

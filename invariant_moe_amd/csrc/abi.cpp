@@ -3,6 +3,7 @@
 // include/moe.h.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -390,6 +391,48 @@ int moe_combine(const void* expert_out, const int32_t* topk_idx, const float* to
   return hip_status(moe::launch_combine(expert_out, topk_idx, topk_w, pair_row, shared_out, T, k,
                                         D, act, y, static_cast<hipStream_t>(stream)),
                     "combine");
+}
+
+static int check_norm(int64_t T, int D, float eps, const void* x, const void* residual,
+                      const void* gamma, const void* residual_out, const void* normed) {
+  if (T < 0) return fail(MOE_ERR_SHAPE, "T must be >= 0");
+  if (D < 32 || D % 32) return fail(MOE_ERR_SHAPE, "D=%d must be a positive multiple of 32", D);
+  if (!(eps >= 0.0f) || !std::isfinite(eps))
+    return fail(MOE_ERR_UNSUPPORTED, "eps must be finite and >= 0");
+  if (T > 0 && (!x || !residual || !gamma || !residual_out || !normed))
+    return fail(MOE_ERR_NULL, "NULL argument");
+  if (T > 0 && (!aligned(x, 16) || !aligned(residual, 16) || !aligned(gamma, 16) ||
+                !aligned(residual_out, 16) || !aligned(normed, 16)))
+    return fail(MOE_ERR_ALIGN, "rows and gamma must be 16-byte aligned");
+  return MOE_OK;
+}
+
+int moe_residual_rmsnorm(const void* x, const void* residual, const void* gamma, float eps,
+                         int64_t T, int D, moe_dtype act, void* residual_out, void* normed,
+                         void* stream) {
+  int rc;
+  if ((rc = check_act(act))) return rc;
+  if ((rc = check_norm(T, D, eps, x, residual, gamma, residual_out, normed))) return rc;
+  return hip_status(moe::launch_residual_rmsnorm(x, residual, gamma, eps, T, D, act, residual_out,
+                                                 normed, static_cast<hipStream_t>(stream)),
+                    "residual_rmsnorm");
+}
+
+int moe_combine_rmsnorm(const void* expert_out, const int32_t* topk_idx, const float* topk_w,
+                        const int32_t* pair_row, const void* shared_out, const void* residual,
+                        const void* gamma, float eps, int64_t T, int k, int D, moe_dtype act,
+                        void* residual_out, void* normed, void* stream) {
+  int rc;
+  if ((rc = check_act(act))) return rc;
+  if (k < 1 || k > MOE_MAX_TOPK) return fail(MOE_ERR_SHAPE, "k=%d out of range", k);
+  if ((rc = check_norm(T, D, eps, expert_out, residual, gamma, residual_out, normed))) return rc;
+  if (T > 0 && (!topk_idx || !topk_w || !pair_row)) return fail(MOE_ERR_NULL, "NULL argument");
+  if (T > 0 && shared_out && !aligned(shared_out, 16))
+    return fail(MOE_ERR_ALIGN, "shared_out must be 16-byte aligned");
+  return hip_status(moe::launch_combine_rmsnorm(expert_out, topk_idx, topk_w, pair_row, shared_out,
+                                                residual, gamma, eps, T, k, D, act, residual_out,
+                                                normed, static_cast<hipStream_t>(stream)),
+                    "combine_rmsnorm");
 }
 
 size_t moe_layer_workspace_bytes(int64_t T, int D, int E, int k, int I, int I_shared,

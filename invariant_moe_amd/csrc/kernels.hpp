@@ -119,5 +119,15 @@ hipError_t launch_grouped_gemm(const GemmPlan& p, const GemmArgs& a, int4* table
 hipError_t launch_combine(const void* expert_out, const int32_t* topk_idx, const float* topk_w,
                           const int32_t* pair_row, const void* shared_out, int64_t T, int k,
                           int D, int act, void* y, hipStream_t s);
+// Residual add + RMSNorm (one workgroup per token); the second form computes
+// its input rows as launch_combine does, without writing them.
+hipError_t launch_residual_rmsnorm(const void* x, const void* residual, const void* gamma,
+                                   float eps, int64_t T, int D, int act, void* residual_out,
+                                   void* normed, hipStream_t s);
+hipError_t launch_combine_rmsnorm(const void* expert_out, const int32_t* topk_idx,
+                                  const float* topk_w, const int32_t* pair_row,
+                                  const void* shared_out, const void* residual, const void* gamma,
+                                  float eps, int64_t T, int k, int D, int act, void* residual_out,
+                                  void* normed, hipStream_t s);
 
 }  // namespace moe

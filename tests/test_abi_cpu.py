@@ -130,3 +130,24 @@ def test_other_entry_points_reject():
     assert L.moe_router_topk(_fake(), 1, _fake(), None, None, 4, 64, 8, 2, 2, _fake(), _fake(),
                              None, 0, None) == -1  # hash needs token ids
     assert L.moe_routing_scores(_fake(), 4, 2, _fake(), None) == -2
+
+
+def test_norm_entry_points_reject():
+    L = moe.lib()
+    f = _fake()
+    # moe_residual_rmsnorm(x, residual, gamma, eps, T, D, act, residual_out, normed, stream)
+    assert L.moe_residual_rmsnorm(f, f, f, 1e-6, 0, 64, 1, f, f, None) == 0  # T = 0: no-op
+    assert L.moe_residual_rmsnorm(f, f, f, 1e-6, 4, 48, 1, f, f, None) == -2  # D % 32
+    assert L.moe_residual_rmsnorm(f, f, f, -1.0, 4, 64, 1, f, f, None) == -6  # eps < 0
+    assert L.moe_residual_rmsnorm(f, f, f, float("inf"), 4, 64, 1, f, f, None) == -6
+    assert L.moe_residual_rmsnorm(f, f, f, float("nan"), 4, 64, 1, f, f, None) == -6
+    assert L.moe_residual_rmsnorm(f, None, f, 1e-6, 4, 64, 1, f, f, None) == -1
+    assert L.moe_residual_rmsnorm(f, f, _fake(0x100008), 1e-6, 4, 64, 1, f, f, None) == -4
+    assert L.moe_residual_rmsnorm(f, f, f, 1e-6, 4, 64, 2, f, f, None) == -3  # MXFP4 rows
+    # moe_combine_rmsnorm(eo, idx, w, pair_row, shared, residual, gamma, eps, T, k, D, act, ro, n)
+    assert L.moe_combine_rmsnorm(f, f, f, f, None, f, f, 1e-6, 4, 0, 64, 1, f, f, None) == -2
+    assert L.moe_combine_rmsnorm(f, f, f, f, None, f, f, 1e-6, 4, 33, 64, 1, f, f, None) == -2
+    assert L.moe_combine_rmsnorm(f, None, f, f, None, f, f, 1e-6, 4, 2, 64, 1, f, f, None) == -1
+    assert L.moe_combine_rmsnorm(f, f, f, f, _fake(0x100004), f, f, 1e-6, 4, 2, 64, 1, f, f,
+                                 None) == -4
+    assert L.moe_combine_rmsnorm(f, f, f, f, None, f, f, -0.5, 4, 2, 64, 1, f, f, None) == -6
