@@ -61,6 +61,10 @@ def lib():
                                      i32]
         L.orc_combine.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i32, vp]
         L.orc_residual_rmsnorm.argtypes = [vp, vp, vp, ctypes.c_double, i64, i32, i32, vp, vp]
+        L.orc_e4m3_value.argtypes, L.orc_e4m3_value.restype = [ctypes.c_uint8], ctypes.c_double
+        L.orc_e4m3_round.argtypes, L.orc_e4m3_round.restype = [ctypes.c_double], ctypes.c_uint8
+        L.orc_mx_e4m3_quantize.argtypes = [vp, i64, i64, vp, vp]
+        L.orc_expert_ffn_w4a8.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32]
         L.orc_layer_forward.argtypes = [vp, i32, vp, vp, vp, ctypes.POINTER(_Experts), vp, vp, vp,
                                         i64, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, i32]
         L.orc_layer_forward.restype = i32
@@ -162,6 +166,40 @@ def expert_ffn(x_rows: np.ndarray, gate, up, down, wdtype: str, want_h=False, gl
     h = np.empty((M, I), dtype=x_rows.dtype) if want_h else None
     lib().orc_expert_ffn(_p(x_rows), ACT[act], M, D, I, WDT[wdtype], _p(g), _p(u), _p(d),
                          _p(gs), _p(us), _p(ds), _p(out), _p(h), GLU[glu])
+    return (out, h) if want_h else out
+
+
+def e4m3_value(code: int) -> float:
+    """OCP FP8 E4M3 (no infinities) value of a code byte."""
+    return lib().orc_e4m3_value(code)
+
+
+def e4m3_round(v: float) -> int:
+    """Nearest E4M3 code, ties to even, saturating at 448."""
+    return lib().orc_e4m3_round(v)
+
+
+def mx_e4m3_quantize(x: np.ndarray):
+    """OCP MX quantisation of rows x [rows, n] (n % 32 == 0, any float dtype, taken
+    exactly as double) to E4M3 codes [rows, n] and E8M0 scales [rows, n/32]."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    rows, n = x.shape
+    codes = np.empty((rows, n), np.uint8)
+    scales = np.empty((rows, n // 32), np.uint8)
+    lib().orc_mx_e4m3_quantize(_p(x), rows, n, _p(codes), _p(scales))
+    return codes, scales
+
+
+def expert_ffn_w4a8(x_rows: np.ndarray, gate, up, down, want_h=False, glu="swiglu"):
+    """One expert with MXFP4 weights ((codes, scales) pairs) and MXFP8 activations:
+    x_rows bf16 bits [M, D] -> out bf16 bits [M, D] (h [M, I] with want_h)."""
+    M, D = x_rows.shape
+    (g, gs), (u, us), (d, ds) = gate, up, down
+    I = g.shape[0]
+    out = np.empty((M, D), np.uint16)
+    h = np.empty((M, I), np.uint16) if want_h else None
+    lib().orc_expert_ffn_w4a8(_p(np.ascontiguousarray(x_rows, dtype=np.uint16)), M, D, I, _p(g),
+                              _p(u), _p(d), _p(gs), _p(us), _p(ds), _p(out), _p(h), GLU[glu])
     return (out, h) if want_h else out
 
 

@@ -233,6 +233,70 @@ void route_token(const float* logits, const float* bias, int32_t tid, int E, int
   }
 }
 
+/* ---- MXFP8 activations for FP4 x FP8 expert GEMMs ----------------------- */
+/* [DS] 6.2: FP4 (E2M1) expert weights feed an FP8 GEMM (FP4 -> FP8 is exact,
+ * FP4 x FP8 matmul on newer hardware).  The page does not say how the
+ * activations become FP8; this library's reading is OCP MX: E4M3 elements
+ * with one E8M0 scale per 32 consecutive values along K.
+ * E4M3 here is OCP FP8 E4M3 ("FN"): sign, 4 exponent bits with bias 7,
+ * 3 mantissa bits, exponent field 0 subnormal (m/8 * 2^-6), no infinities,
+ * 0x7F / 0xFF NaN, largest finite 448. */
+double e4m3_value(uint8_t c) {
+  const int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  if (e == 15 && m == 7) return std::nan("");
+  const double v = e == 0 ? std::ldexp(m / 8.0, -6) : std::ldexp(1.0 + m / 8.0, e - 7);
+  return s ? -v : v;
+}
+
+/* The E4M3 code nearest to v, ties to the even code (mantissa LSB 0);
+ * magnitudes above 448 saturate to 448 (the MX conversion clamps to the
+ * largest normal); NaN gives 0x7F.  The sign bit is v's, zero included.
+ * Found by searching the finite non-negative codes, which increase with
+ * their value. */
+uint8_t e4m3_round(double v) {
+  if (std::isnan(v)) return 0x7f;
+  double a = std::fabs(v);
+  if (a > 448.0) a = 448.0;
+  int best = 0;
+  double bd = a;
+  for (int c = 1; c <= 0x7e; ++c) {
+    const double d = std::fabs(a - e4m3_value((uint8_t)c));
+    if (d < bd || (d == bd && (c & 1) == 0)) {
+      best = c;
+      bd = d;
+    }
+  }
+  return (uint8_t)(best | (std::signbit(v) ? 0x80 : 0));
+}
+
+/* One block of 32 (OCP MX): X = floor(log2(amax)) - 8, 8 being the exponent
+ * of E4M3's largest power of two, as the E8M0 byte X + 127 clamped to
+ * [0, 254]; codes = e4m3_round(x / 2^X).  amax = 0 (no finite nonzero
+ * value) gives the byte 0. */
+void mx_e4m3_block(const double* x, uint8_t* codes, uint8_t* scale) {
+  double amax = 0.0;
+  for (int i = 0; i < 32; ++i)
+    if (std::isfinite(x[i]) && std::fabs(x[i]) > amax) amax = std::fabs(x[i]);
+  int byte = 0;
+  if (amax > 0.0) {
+    int e;
+    std::frexp(amax, &e);  // amax = f * 2^e, f in [0.5, 1): floor(log2(amax)) = e - 1
+    byte = std::min(254, std::max(0, (e - 1) - 8 + 127));
+  }
+  *scale = (uint8_t)byte;
+  for (int i = 0; i < 32; ++i) codes[i] = e4m3_round(std::ldexp(x[i], 127 - byte));
+}
+
+/* Row of n values (n % 32 == 0) quantised and dequantised: the values an
+ * FP4 x FP8 GEMM sees. */
+void mx_e4m3_dequantised_row(const double* x, int64_t n, double* out) {
+  uint8_t codes[32], scale;
+  for (int64_t b = 0; b < n; b += 32) {
+    mx_e4m3_block(x + b, codes, &scale);
+    for (int i = 0; i < 32; ++i) out[b + i] = std::ldexp(e4m3_value(codes[i]), (int)scale - 127);
+  }
+}
+
 /* Gated activation a(g, u) of the expert FFN from the gate branch g = W_g x
  * and the up branch u = W_u x, in double:
  *  GLU_SWIGLU  SiLU(g) * u, SiLU(g) = g * sigmoid(g)        ([DS] 6.5; [LD] GLU branches)
@@ -360,6 +424,52 @@ int orc_permute(const int32_t* topk_idx, int64_t T, int k, int E, int32_t* count
       pair_row[t * k + j] = r;
     }
   return 0;
+}
+
+/* ---- MXFP8 helpers and the FP4 x FP8 expert FFN ------------------------- */
+double orc_e4m3_value(uint8_t c) { return e4m3_value(c); }
+uint8_t orc_e4m3_round(double v) { return e4m3_round(v); }
+/* x [rows, n] (n % 32 == 0) -> codes [rows, n], scales [rows, n/32]. */
+void orc_mx_e4m3_quantize(const double* x, int64_t rows, int64_t n, uint8_t* codes,
+                          uint8_t* scales) {
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t b = 0; b < n; b += 32)
+      mx_e4m3_block(x + r * n + b, codes + r * n + b, scales + r * (n / 32) + b / 32);
+}
+
+/* One expert over M rows with MXFP4 weights and MXFP8 activations ([DS] 6.2
+ * FP4 x FP8): x rows (bf16) are quantised per 32 along D before the gate/up
+ * GEMM, and the rounded h rows per 32 along I before the down GEMM; the
+ * GEMMs are exact (double) on the dequantised values; rounding points as in
+ * expert_ffn (h and out bf16).  glu as in glu_value. */
+void orc_expert_ffn_w4a8(const uint16_t* x_rows, int64_t M, int D, int I, const uint8_t* gate,
+                         const uint8_t* up, const uint8_t* down, const uint8_t* gate_scale,
+                         const uint8_t* up_scale, const uint8_t* down_scale, uint16_t* out,
+                         uint16_t* h_out, int glu) {
+  const std::vector<double> Wg = weight_matrix(gate, gate_scale, W_MXFP4, I, D);
+  const std::vector<double> Wu = weight_matrix(up, up_scale, W_MXFP4, I, D);
+  const std::vector<double> Wd = weight_matrix(down, down_scale, W_MXFP4, D, I);
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < M; ++r) {
+    std::vector<double> x((size_t)D), xq((size_t)D), h((size_t)I), hq((size_t)I);
+    for (int d = 0; d < D; ++d) x[(size_t)d] = bf16_value(x_rows[r * D + d]);
+    mx_e4m3_dequantised_row(x.data(), D, xq.data());
+    for (int i = 0; i < I; ++i) {
+      double g = 0.0, u = 0.0;
+      for (int d = 0; d < D; ++d) {
+        g += xq[(size_t)d] * Wg[(size_t)i * D + d];
+        u += xq[(size_t)d] * Wu[(size_t)i * D + d];
+      }
+      h[(size_t)i] = bf16_value(bf16_round(glu_value(g, u, glu)));
+      if (h_out) h_out[r * I + i] = bf16_round(h[(size_t)i]);
+    }
+    mx_e4m3_dequantised_row(h.data(), I, hq.data());
+    for (int n = 0; n < D; ++n) {
+      double o = 0.0;
+      for (int i = 0; i < I; ++i) o += hq[(size_t)i] * Wd[(size_t)n * I + i];
+      out[r * D + n] = bf16_round(o);
+    }
+  }
 }
 
 /* ---- one expert's SwiGLU FFN over M rows (DS 6.5 SwiGLU; LD GLU branches) */
