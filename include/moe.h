@@ -201,6 +201,39 @@ int moe_grouped_swiglu(const void* x_rows, const int32_t* row_index,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * FP4 x FP8 expert compute (W4A8; [DS] 6.2: FP4 expert weights run in an FP8
+ * GEMM).  The page does not say how activations become FP8; the reading here
+ * is OCP MX: E4M3 elements (OCP FP8, bias 7, no infinities, largest 448) with
+ * one E8M0 scale per 32 consecutive values along K:
+ *   X = floor(log2(max |v| over the block's finite values)) - 8, scale byte
+ *   X + 127 clamped to [0, 254] (byte 0 when the block has no finite nonzero
+ *   value); element = the E4M3 code nearest to v / 2^X, ties to the even
+ *   code, magnitudes past 448 clamped to 448 with their sign, NaN -> 0x7F.
+ *
+ * moe_mx_e4m3_quantize: R bf16 rows of K (K % 32 == 0) -> codes [R, K] u8 and
+ *   scales [R, K/32] u8; row r reads x[row_index[r]] (row_index NULL: x[r]).
+ *   x 16-byte aligned, codes 8-byte aligned.
+ *
+ * moe_grouped_swiglu_w4a8: moe_grouped_swiglu with MXFP4 weights and MXFP8
+ *   activations.  The rows x_rows[row_index[r]] are quantised per 32 along D,
+ *   the gate/up GEMM runs on gfx950's scaled FP4 x FP8 MFMA (both block scales
+ *   applied in the instruction, fp32 accumulation, K stepped by 128 in
+ *   increasing order from 0 for every row), h = round_bf16(glu(g, u)) is
+ *   quantised per 32 along I, and the down GEMM gives out = round_bf16(W_down h).
+ *   Every output row depends only on its own input row, whatever R or E.
+ *   w: MXFP4 (codes + scales); x_rows, out bf16.  D and I multiples of 128.
+ *   flags: 0, MOE_FLAG_GLU_CLAMP or MOE_FLAG_GLU_SITU.
+ *   workspace: moe_grouped_swiglu_w4a8_workspace_bytes(R, E, D, I) bytes.
+ * ------------------------------------------------------------------------- */
+int moe_mx_e4m3_quantize(const void* x, const int32_t* row_index, int64_t R, int K,
+                         uint8_t* codes, uint8_t* scales, void* stream);
+size_t moe_grouped_swiglu_w4a8_workspace_bytes(int64_t R, int E, int D, int I);
+int moe_grouped_swiglu_w4a8(const void* x_rows, const int32_t* row_index,
+                            const int32_t* expert_offsets, int64_t R, int E, int D, int I,
+                            const moe_expert_weights* w, uint32_t flags, void* out,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * moe_combine — the MoE finalize ([FW] trap 3 and case study):
  *   acc = +0; for each of token t's experts in ascending expert id:
  *       acc = fmaf(topk_w[t,j], float(expert_out[pair_row[t*k+j]]), acc)

@@ -24,6 +24,8 @@ GLU = {"swiglu": 0, "clamp": 0x1, "situ": 0x2}
 STAGES = ("routing", "permute", "gate_up_gemm", "down_gemm", "combine")
 EXPORTS = ("moe_router_workspace_bytes", "moe_router_topk", "moe_routing_scores", "moe_permute_workspace_bytes",
            "moe_permute", "moe_grouped_swiglu_workspace_bytes", "moe_grouped_swiglu",
+           "moe_mx_e4m3_quantize", "moe_grouped_swiglu_w4a8_workspace_bytes",
+           "moe_grouped_swiglu_w4a8",
            "moe_combine", "moe_residual_rmsnorm", "moe_combine_rmsnorm",
            "moe_layer_workspace_bytes", "moe_layer_forward",
            "moe_set_stage_events", "moe_status_string", "moe_last_error", "moe_abi_version")
@@ -63,6 +65,11 @@ def lib() -> ctypes.CDLL:
         L.moe_grouped_swiglu_workspace_bytes.restype = sz
         L.moe_grouped_swiglu.argtypes = [vp, vp, vp, i64, i32, i32, i32, WP, i32, u32, vp, vp, sz, vp]
         L.moe_combine.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i32, vp, vp]
+        L.moe_mx_e4m3_quantize.argtypes = [vp, vp, i64, i32, vp, vp, vp]
+        L.moe_grouped_swiglu_w4a8_workspace_bytes.argtypes = [i64, i32, i32, i32]
+        L.moe_grouped_swiglu_w4a8_workspace_bytes.restype = sz
+        L.moe_grouped_swiglu_w4a8.argtypes = [vp, vp, vp, i64, i32, i32, i32, WP, u32, vp, vp, sz,
+                                              vp]
         f32 = ctypes.c_float
         L.moe_residual_rmsnorm.argtypes = [vp, vp, vp, f32, i64, i32, i32, vp, vp, vp]
         L.moe_combine_rmsnorm.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32, i64, i32, i32, i32, vp,
@@ -77,6 +84,7 @@ def lib() -> ctypes.CDLL:
         L.moe_last_error.restype = ctypes.c_char_p
         for name in ("moe_router_topk", "moe_routing_scores", "moe_permute", "moe_grouped_swiglu", "moe_combine",
                      "moe_residual_rmsnorm", "moe_combine_rmsnorm", "moe_layer_forward",
+                     "moe_mx_e4m3_quantize", "moe_grouped_swiglu_w4a8",
                      "moe_set_stage_events", "moe_abi_version"):
             getattr(L, name).restype = i32
         _lib = L
@@ -206,6 +214,38 @@ def grouped_swiglu(x_rows, row_index, expert_offsets, R: int, E: int, weights: E
     _check(L.moe_grouped_swiglu(_ptr(x_rows), _ptr(row_index), _ptr(expert_offsets), R, E, D, I,
                                 ctypes.byref(wst), act, GLU[glu], _ptr(out), _ptr(ws), nb,
                                 _stream(stream)))
+    return out
+
+
+def mx_e4m3_quantize(x, row_index=None, R=None, stream=None):
+    """MXFP8 (E4M3 + E8M0 per 32) codes [R, K] and scales [R, K/32] of bf16 rows
+    x[row_index[r]] (or x[r])."""
+    K = x.shape[1]
+    if R is None:
+        R = row_index.shape[0] if row_index is not None else x.shape[0]
+    codes = torch.empty((R, K), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((R, K // 32), dtype=torch.uint8, device=x.device)
+    _check(lib().moe_mx_e4m3_quantize(_ptr(x), _ptr(row_index), R, K, _ptr(codes),
+                                      _ptr(scales), _stream(stream)))
+    return codes, scales
+
+
+def grouped_swiglu_w4a8(x_rows, row_index, expert_offsets, R: int, E: int,
+                        weights: ExpertWeights, out=None, stream=None, glu: str = "swiglu"):
+    """Expert FFN over grouped rows with MXFP4 weights and MXFP8 activations:
+    out [R, D] bf16."""
+    D = x_rows.shape[1]
+    I = weights.gate.shape[1]
+    if out is None:
+        out = torch.empty((R, D), dtype=x_rows.dtype, device=x_rows.device)
+    L = lib()
+    nb = L.moe_grouped_swiglu_w4a8_workspace_bytes(R, E, D, I)
+    ws = _workspace(nb + 256, x_rows.device)
+    wp = (ws.data_ptr() + 255) // 256 * 256
+    wst = weights.as_struct()
+    _check(L.moe_grouped_swiglu_w4a8(_ptr(x_rows), _ptr(row_index), _ptr(expert_offsets), R, E,
+                                     D, I, ctypes.byref(wst), GLU[glu], _ptr(out), wp,
+                                     ws.numel() - (wp - ws.data_ptr()), _stream(stream)))
     return out
 
 

@@ -26,7 +26,7 @@ DEVICE_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-result",
 ]
-SOURCES = ["router.hip", "permute.hip", "gemm.hip", "combine.hip", "abi.cpp"]
+SOURCES = ["router.hip", "permute.hip", "gemm.hip", "combine.hip", "quant.hip", "abi.cpp"]
 
 
 def _compile(src: str) -> str:

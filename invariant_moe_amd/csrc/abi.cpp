@@ -375,6 +375,113 @@ int moe_grouped_swiglu(const void* x_rows, const int32_t* row_index, const int32
   return hip_status(e, "grouped_swiglu");
 }
 
+int moe_mx_e4m3_quantize(const void* x, const int32_t* row_index, int64_t R, int K,
+                         uint8_t* codes, uint8_t* scales, void* stream) {
+  if (R < 0 || R >= ((int64_t)1 << 31)) return fail(MOE_ERR_SHAPE, "R out of range");
+  if (K < 32 || K % 32) return fail(MOE_ERR_SHAPE, "K=%d must be a positive multiple of 32", K);
+  if (R > 0 && (!x || !codes || !scales)) return fail(MOE_ERR_NULL, "NULL argument");
+  if (R > 0 && (!aligned(x, 16) || !aligned(codes, 8)))
+    return fail(MOE_ERR_ALIGN, "x must be 16-byte and codes 8-byte aligned");
+  return hip_status(moe::launch_mx_e4m3_quantize(x, row_index, R, K, codes, scales,
+                                                 static_cast<hipStream_t>(stream)),
+                    "mx_e4m3_quantize");
+}
+
+// x codes + scales, h (bf16), h codes + scales, then the two GEMMs' tile tables.
+static int64_t w4a8_table_entries(int64_t R, int E, int D, int I) {
+  moe::SegShape up{true, R, E, D, I, 2}, dn{true, R, E, I, D, 2};
+  return moe::plan_table_entries(moe::plan_w4a8_gemm(up, true)) +
+         moe::plan_table_entries(moe::plan_w4a8_gemm(dn, false));
+}
+
+size_t moe_grouped_swiglu_w4a8_workspace_bytes(int64_t R, int E, int D, int I) {
+  if (R <= 0 || E <= 0 || D <= 0 || I <= 0) return 0;
+  Carver c;
+  c.take((size_t)R * D);
+  c.take((size_t)R * (D / 32));
+  c.take((size_t)R * I * 2);
+  c.take((size_t)R * I);
+  c.take((size_t)R * (I / 32));
+  c.take((size_t)w4a8_table_entries(R, E, D, I) * sizeof(int4));
+  return c.off;
+}
+
+int moe_grouped_swiglu_w4a8(const void* x_rows, const int32_t* row_index,
+                            const int32_t* expert_offsets, int64_t R, int E, int D, int I,
+                            const moe_expert_weights* w, uint32_t flags, void* out,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  int rc, glu;
+  if ((rc = glu_from_flags(flags, &glu))) return rc;
+  if (R < 0 || R >= ((int64_t)1 << 31)) return fail(MOE_ERR_SHAPE, "R out of range");
+  if (E < 1 || E > MOE_MAX_EXPERTS) return fail(MOE_ERR_SHAPE, "E=%d out of range", E);
+  if (D < 128 || D % 128 || I < 128 || I % 128)
+    return fail(MOE_ERR_SHAPE, "D=%d and I=%d must be positive multiples of 128", D, I);
+  if (!w) return fail(MOE_ERR_NULL, "weights are NULL");
+  if (w->dtype != MOE_MXFP4) return fail(MOE_ERR_DTYPE, "FP4 x FP8 needs MXFP4 weights");
+  if ((rc = check_weights(w, MOE_BF16, "expert"))) return rc;
+  if (!expert_offsets || !out || (R > 0 && !x_rows)) return fail(MOE_ERR_NULL, "NULL argument");
+  if ((x_rows && !aligned(x_rows, 16)) || !aligned(out, 16))
+    return fail(MOE_ERR_ALIGN, "x_rows / out misaligned");
+  const size_t need = moe_grouped_swiglu_w4a8_workspace_bytes(R, E, D, I);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(MOE_ERR_WORKSPACE, "grouped_swiglu_w4a8 workspace needs %zu bytes", need);
+  if (workspace && !aligned(workspace, 256)) return fail(MOE_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if (R == 0) return ok();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  moe::SegShape su{true, R, E, D, I, 2}, sd{true, R, E, I, D, 2};
+  const moe::GemmPlan pu = moe::plan_w4a8_gemm(su, true), pd = moe::plan_w4a8_gemm(sd, false);
+  if (!pu.valid || !pd.valid) return fail(MOE_ERR_SHAPE, "problem too large for one launch");
+  char* ws = static_cast<char*>(workspace);
+  Carver c;
+  uint8_t* xq = reinterpret_cast<uint8_t*>(ws + c.take((size_t)R * D));
+  uint8_t* xs = reinterpret_cast<uint8_t*>(ws + c.take((size_t)R * (D / 32)));
+  void* h = ws + c.take((size_t)R * I * 2);
+  uint8_t* hq = reinterpret_cast<uint8_t*>(ws + c.take((size_t)R * I));
+  uint8_t* hs = reinterpret_cast<uint8_t*>(ws + c.take((size_t)R * (I / 32)));
+  int4* tiles_up = reinterpret_cast<int4*>(ws + c.off);
+  int4* tiles_dn = tiles_up + moe::plan_table_entries(pu);
+  moe::TileJobs jobs{};
+  if (!moe::plan_tile_jobs(pu, tiles_up, jobs) || !moe::plan_tile_jobs(pd, tiles_dn, jobs))
+    return fail(MOE_ERR_UNSUPPORTED, "gate/up and down GEMM plans use different row tiles");
+  hipError_t e = moe::launch_tile_tables(expert_offsets, E, jobs, s);
+  if (e == hipSuccess) e = moe::launch_mx_e4m3_quantize(x_rows, row_index, R, D, xq, xs, s);
+  moe::GemmArgs up{};
+  up.nseg = 1;
+  up.glu = glu;
+  moe::GemmSeg& a = up.seg[0];
+  a.A = xq;
+  a.AS = xs;
+  a.offsets = expert_offsets;
+  a.M = R;
+  a.G = E;
+  a.K = D;
+  a.N = I;
+  a.W0 = w->gate;
+  a.W1 = w->up;
+  a.S0 = w->gate_scale;
+  a.S1 = w->up_scale;
+  a.wfmt = 2;
+  a.out = h;
+  if (e == hipSuccess) e = moe::launch_grouped_gemm(pu, up, tiles_up, s);
+  if (e == hipSuccess) e = moe::launch_mx_e4m3_quantize(h, nullptr, R, I, hq, hs, s);
+  moe::GemmArgs dn{};
+  dn.nseg = 1;
+  moe::GemmSeg& b = dn.seg[0];
+  b.A = hq;
+  b.AS = hs;
+  b.offsets = expert_offsets;
+  b.M = R;
+  b.G = E;
+  b.K = I;
+  b.N = D;
+  b.W0 = w->down;
+  b.S0 = w->down_scale;
+  b.wfmt = 2;
+  b.out = out;
+  if (e == hipSuccess) e = moe::launch_grouped_gemm(pd, dn, tiles_dn, s);
+  return hip_status(e, "grouped_swiglu_w4a8");
+}
+
 int moe_combine(const void* expert_out, const int32_t* topk_idx, const float* topk_w,
                 const int32_t* pair_row, const void* shared_out, int64_t T, int k, int D,
                 moe_dtype act, void* y, void* stream) {

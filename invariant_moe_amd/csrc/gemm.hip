@@ -529,6 +529,190 @@ __global__ __launch_bounds__(256) void k_grouped_gemm_f32(GemmArgs args) {
 }
 
 // ---------------------------------------------------------------------------
+// FP4 x FP8 kernel (W4A8; the DeepSeek-V4 walkthrough, section 6.2, runs FP4
+// expert weights in an FP8 GEMM): MXFP4 weights as operand A and MXFP8 token
+// rows (E4M3 + E8M0 per 32, quant.hip) as operand B of gfx950's
+// v_mfma_scale_f32_16x16x128_f8f6f4, which applies both E8M0 block scales
+// itself.  K steps by 128 in increasing order from a zero accumulator, one
+// instruction per (16 features, 16 tokens, 128 of K): one chain per output
+// element whatever the tile, so T changes no bit.
+// Operand layout (measured on MI355X with one-hot operands):
+//   A (E2M1, 4 VGPRs): lane 16g + i holds weight row i, K 32g .. 32g+31,
+//       element e in nibble e (low nibble first);
+//   B (E4M3, 8 VGPRs): lane 16g + j holds token row j, K 16g .. 16g+15 in
+//       bytes 0..15 and K 64+16g .. 64+16g+15 in bytes 16..31;
+//   scales: lane 16b + i (A) or 16b + j (B) passes the E8M0 byte of K block b
+//       (K 32b .. 32b+31) of its row in bits 0..7;
+//   result: lane l, element v is feature 4(l/16) + v, token l % 16, as for
+//       the bf16 MFMA above.
+// LDS: token rows of a stage are 128 bytes, weight rows 64 bytes paired into
+// 128-byte lines; 16-byte chunks XOR-swizzled by line as in lds_off.
+// ---------------------------------------------------------------------------
+constexpr int KQ = 128;  // K per stage
+
+__device__ __forceinline__ int lds_line_off(int line, int chunk) {
+  return line * 128 + ((chunk ^ (line & 7)) << 4);
+}
+
+template <int BM, int BN, int WM, int WN, bool GATED>
+__global__ __launch_bounds__(64 * WM * WN, 2) void k_grouped_gemm_w4a8(GemmArgs args) {
+  constexpr int NT = 64 * WM * WN;
+  constexpr int NMAT = GATED ? 2 : 1;
+  constexpr int TBW = BM / 16 / WM;
+  constexpr int NBW = BN / 16 / WN;
+  static_assert(TBW >= 1 && NBW >= 1, "tile too small for the wave grid");
+  constexpr int XCH = BM * 8;         // 16-byte chunks of a token stage
+  constexpr int WCH = NMAT * BN * 4;  // 16-byte chunks of a weight stage
+  constexpr int XPT = (XCH + NT - 1) / NT;
+  constexpr int WPT = (WCH + NT - 1) / NT;
+  __shared__ __align__(16) uint8_t sx[2][BM * 128];
+  __shared__ __align__(16) uint8_t sw[2][NMAT * BN * 64];
+  __shared__ uint32_t ssx[2][BM];
+  __shared__ uint32_t ssw[2][NMAT * BN];
+
+  TileInfo ti;
+  if (!read_tile(args, BM, ti)) return;
+  const GemmSeg& s = args.seg[ti.seg];
+  const int K = s.K, N = s.N, nst = K / KQ;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const uint8_t* X = static_cast<const uint8_t*>(s.A);
+
+  // sources: token chunk c = (row, 16-byte chunk), weight chunk c = (mat, row, chunk)
+  const uint8_t* xsrc[XPT];
+  const uint8_t* wsrc[WPT];
+#pragma unroll
+  for (int i = 0; i < XPT; ++i) {
+    const int c = min(tid + i * NT, XCH - 1);
+    const int r = min(c / 8, ti.rows - 1);
+    int64_t row = ti.row0 + r;
+    if (s.a_index) row = s.a_index[row];
+    xsrc[i] = X + row * K + (c % 8) * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    const int c = min(tid + i * NT, WCH - 1);
+    const int mat = c / (BN * 4), n = (c / 4) % BN;
+    const int nn = min(ti.n0 + n, N - 1);
+    const uint8_t* base = static_cast<const uint8_t*>(mat ? s.W1 : s.W0);
+    wsrc[i] = base + ((int64_t)ti.g * N + nn) * (K / 2) + (c % 4) * 16;
+  }
+  // scale words (the 4 E8M0 bytes of one row's stage): tokens by threads
+  // 0..BM-1, weight rows by threads BM..BM+NMAT*BN-1
+  const uint8_t* scsrc = nullptr;
+  if (tid < BM) {
+    int64_t row = ti.row0 + min(tid, ti.rows - 1);
+    if (s.a_index) row = s.a_index[row];
+    scsrc = s.AS + row * (K / 32);
+  } else if (tid < BM + NMAT * BN) {
+    const int c = tid - BM, mat = c / BN, nn = min(ti.n0 + c % BN, N - 1);
+    scsrc = (mat ? s.S1 : s.S0) + ((int64_t)ti.g * N + nn) * (K / 32);
+  }
+
+  f32x4_t acc[NMAT][NBW][TBW];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+      for (int tb = 0; tb < TBW; ++tb) acc[m][nb][tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // native: plain loads and stores
+  u32x4 xr[XPT], wr[WPT];
+  uint32_t sc = 127u;
+  // stage loads into registers, then into LDS (the arrays are passed, not
+  // captured, so that they stay in registers)
+  auto gload = [&](u32x4 (&xq)[XPT], u32x4 (&wq)[WPT], uint32_t& scq, int kt) {
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) xq[i] = *reinterpret_cast<const u32x4*>(xsrc[i] + kt * KQ);
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) wq[i] = *reinterpret_cast<const u32x4*>(wsrc[i] + kt * (KQ / 2));
+    if (scsrc) scq = *reinterpret_cast<const uint32_t*>(scsrc + kt * 4);
+  };
+  auto lstore = [&](const u32x4 (&xq)[XPT], const u32x4 (&wq)[WPT], uint32_t scq, int buf) {
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      const int c = tid + i * NT;
+      if (c < XCH)
+        *reinterpret_cast<u32x4*>(&sx[buf][lds_line_off(c / 8, c % 8)]) = xq[i];
+    }
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) {
+      const int c = tid + i * NT;
+      if (c < WCH) {
+        const int wrow = c / 4;  // mat * BN + n
+        *reinterpret_cast<u32x4*>(&sw[buf][lds_line_off(wrow >> 1, ((wrow & 1) << 2) | (c % 4))]) =
+            wq[i];
+      }
+    }
+    if (tid < BM)
+      ssx[buf][tid] = scq;
+    else if (tid < BM + NMAT * BN)
+      ssw[buf][tid - BM] = scq;
+  };
+  const int g4 = lane >> 4, r16 = lane & 15;
+  auto compute = [&](int buf) {
+    typedef int v8i __attribute__((ext_vector_type(8)));
+    v8i bfr[TBW];
+    int bsc[TBW];
+#pragma unroll
+    for (int tb = 0; tb < TBW; ++tb) {
+      const int trow = (wm * TBW + tb) * 16 + r16;
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(&sx[buf][lds_line_off(trow, g4)]);
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(&sx[buf][lds_line_off(trow, 4 + g4)]);
+      bfr[tb] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                    (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      bsc[tb] = (int)((ssx[buf][trow] >> (8 * g4)) & 0xffu);
+    }
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb) {
+        const int wrow = m * BN + (wn * NBW + nb) * 16 + r16;
+        const u32x4 q =
+            *reinterpret_cast<const u32x4*>(&sw[buf][lds_line_off(wrow >> 1, ((wrow & 1) << 2) | g4)]);
+        const v8i afr = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+        const int asc = (int)((ssw[buf][wrow] >> (8 * g4)) & 0xffu);
+#pragma unroll
+        for (int tb = 0; tb < TBW; ++tb)
+          acc[m][nb][tb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              afr, bfr[tb], acc[m][nb][tb], 4, 0, 0, asc, 0, bsc[tb]);
+      }
+  };
+
+  gload(xr, wr, sc, 0);
+  lstore(xr, wr, sc, 0);
+  __syncthreads();
+  for (int kt = 0; kt < nst; ++kt) {
+    const bool more = kt + 1 < nst;  // uniform
+    if (more) gload(xr, wr, sc, kt + 1);
+    compute(kt & 1);
+    if (more) lstore(xr, wr, sc, (kt + 1) & 1);
+    __syncthreads();
+  }
+
+  // epilogue (as the bf16 kernel): features n = base + 4*(lane/16) + v of token
+  // row base + lane%16 -> one 8-byte store of 4 bf16
+  uint16_t* out = static_cast<uint16_t*>(s.out);
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+    for (int tb = 0; tb < TBW; ++tb) {
+      const int r = (wm * TBW + tb) * 16 + r16;
+      const int n = ti.n0 + (wn * NBW + nb) * 16 + 4 * g4;
+      if (r < ti.rows && n < N) {
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          v[i] = GATED ? glu_act<FastMath>(acc[0][nb][tb][i], acc[NMAT - 1][nb][tb][i], args.glu)
+                       : acc[0][nb][tb][i];
+        uint2 pk = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        *reinterpret_cast<uint2*>(out + (ti.row0 + r) * (int64_t)N + n) = pk;
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Host planning and launch.  The grid of a launch is an upper bound of its
 // tile count known without a device sync; surplus workgroups read an empty
 // descriptor and exit.
@@ -565,7 +749,8 @@ enum TileCfg {
   TILE_128x128_2x2_P2,    // prefill
   TILE_128x128_2x4_P2,    // prefill gate/up: 8 waves, two per SIMD
   TILE_COUNT,
-  TILE_F32 = 100          // fp32 VALU kernel, 16 x 16 tiles
+  TILE_F32 = 100,         // fp32 VALU kernel, 16 x 16 tiles
+  TILE_W4A8 = 200         // FP4 x FP8 kernel, 64 x 64 tiles on 2 x 2 waves
 };
 
 struct TileShape {
@@ -582,6 +767,7 @@ static TileShape tile_shape(int cfg) {
     case TILE_128x64_2x2_P2: return {128, 64};
     case TILE_128x128_2x2_P2: return {128, 128};
     case TILE_128x128_2x4_P2: return {128, 128};
+    case TILE_W4A8: return {64, 64};
     default: return {16, 16};  // TILE_F32
   }
 }
@@ -673,6 +859,24 @@ GemmPlan plan_grouped_gemm(const SegShape* segs, int nseg, bool gated, int act,
   return p;
 }
 
+GemmPlan plan_w4a8_gemm(const SegShape& seg, bool gated) {
+  GemmPlan p{};
+  p.valid = true;
+  p.gated = gated;
+  p.act = MOE_BF16;
+  p.nseg = 1;
+  p.seg[0] = seg;
+  PlanLaunch& L = p.l[0];
+  L.seg_mask = 1;
+  L.cfg = TILE_W4A8;
+  L.BM = 64;
+  L.BN = 64;
+  L.grid = (seg_tile_bound(seg, 64, 64) + 7) / 8 * 8;
+  if (L.grid > 0x7ffffff8) p.valid = false;
+  if (L.grid > 0) p.n = 1;
+  return p;
+}
+
 int64_t plan_table_entries(const GemmPlan& p) {
   int64_t n = 0;
   for (int i = 0; i < p.n; ++i) n += p.l[i].grid;
@@ -713,7 +917,15 @@ hipError_t launch_grouped_gemm(const GemmPlan& p, const GemmArgs& a, int4* table
     one.glu = a.glu;
     const LaunchEvents ev{i == 0 ? ev_start : nullptr, i == p.n - 1 ? ev_stop : nullptr};
     hipError_t e;
-    if (L.cfg == TILE_F32) {
+    if (L.cfg == TILE_W4A8) {
+      if (p.gated)
+        hipExtLaunchKernelGGL((k_grouped_gemm_w4a8<64, 64, 2, 2, true>), dim3((unsigned)L.grid),
+                              dim3(256), 0, st, ev.start, ev.stop, 0, one);
+      else
+        hipExtLaunchKernelGGL((k_grouped_gemm_w4a8<64, 64, 2, 2, false>), dim3((unsigned)L.grid),
+                              dim3(256), 0, st, ev.start, ev.stop, 0, one);
+      e = hipGetLastError();
+    } else if (L.cfg == TILE_F32) {
       if (p.gated)
         hipExtLaunchKernelGGL(k_grouped_gemm_f32<true>, dim3((unsigned)L.grid), dim3(256), 0, st,
                               ev.start, ev.stop, 0, one);

@@ -23,6 +23,7 @@ struct GemmSeg {
   const uint8_t* S1;
   int wfmt;                // 0 bf16/fp32 (as act), 1 MXFP4
   void* out;               // [rows, N]
+  const uint8_t* AS;       // FP4 x FP8 launches: A is E4M3 codes [*, K], AS E8M0 [*, K/32]
 };
 
 // Tile descriptor, one per workgroup of a GEMM launch (int4):
@@ -102,6 +103,13 @@ hipError_t launch_gather_rows(const void* x, const int32_t* row_token, int64_t T
                               int64_t row_bytes, void* out, hipStream_t s);
 // Tile tables from caller-supplied offsets [E+1] (one small launch).
 hipError_t launch_tile_tables(const int32_t* offsets, int E, const TileJobs& jobs, hipStream_t s);
+
+// MXFP8 activation quantisation (E4M3 + E8M0 per 32 along K) of R bf16 rows
+// of K (K % 32 == 0); row r reads x[row_index[r]] (row_index NULL: x[r]).
+hipError_t launch_mx_e4m3_quantize(const void* x, const int32_t* row_index, int64_t R, int K,
+                                   uint8_t* codes, uint8_t* scales, hipStream_t s);
+// Plan of an FP4 x FP8 grouped GEMM (one segment of MXFP4 weights, K % 128 == 0).
+GemmPlan plan_w4a8_gemm(const SegShape& seg, bool gated);
 
 // Host planning of a grouped GEMM (tile shape, launches, table sizes).
 GemmPlan plan_grouped_gemm(const SegShape* segs, int nseg, bool gated, int act,
