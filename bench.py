@@ -28,6 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA (FP4 x FP8 runs at the FP8 rate)
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "gate_up_gemm_traffic.json")
@@ -214,6 +215,50 @@ def tail_measurement(cfg, hip, sptr, steps: int):
             "kernel": "k_residual_rmsnorm (combine fused with residual add + RMSNorm)"}
 
 
+def w4a8_measurement(dl, x, ids, hip, sptr, steps: int):
+    """The routed expert FFN of an MXFP4-weight workload, on this batch's routed
+    rows: bf16 activations (MXFP4 decoded to bf16, bf16 MFMA) against MXFP8
+    activations on the scaled FP4 x FP8 MFMA (moe_grouped_swiglu_w4a8)."""
+    import torch
+
+    import invariant_moe_amd as moe
+
+    cfg = dl.cfg
+    T, D, E, k, I = cfg.T, cfg.D, cfg.E, cfg.k, cfg.I
+    R = T * k
+    idx, _ = moe.router_topk(x, dl.w_router, dl.bias, ids, E, k, cfg.route)
+    _, offsets, row_token, _, _ = moe.permute(idx, E)
+    w = moe.ExpertWeights(dl.gate, dl.up, dl.down, dl.gate_scale, dl.up_scale, dl.down_scale)
+    out = torch.empty((R, D), dtype=x.dtype, device=x.device)
+
+    def w4a16():
+        moe.grouped_swiglu(x, row_token, offsets, R, E, w, out=out)
+
+    def w4a8():
+        moe.grouped_swiglu_w4a8(x, row_token, offsets, R, E, w, out=out)
+
+    res = {}
+    for name, fn in (("w4a16", w4a16), ("w4a8", w4a8)):
+        for _ in range(3):
+            fn()
+        a, b = hip.event(), hip.event()
+        torch.cuda.synchronize()
+        hip.record(a, sptr)
+        for _ in range(steps):
+            fn()
+        hip.record(b, sptr)
+        torch.cuda.synchronize()
+        res[name] = hip.elapsed_ms(a, b) / steps
+    flops = 6 * R * D * I
+    return {"w4a16_ms": round(res["w4a16"], 4), "w4a8_ms": round(res["w4a8"], 4),
+            "w4a16_tflops": round(flops / (res["w4a16"] * 1e-3) / 1e12, 1),
+            "w4a8_tflops": round(flops / (res["w4a8"] * 1e-3) / 1e12, 1),
+            "w4a8_frac_of_fp8_peak": round(flops / (res["w4a8"] * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
+            "rows": R, "includes": "activation quantisation, tile tables, both GEMMs",
+            "kernel": "k_grouped_gemm_w4a8 (v_mfma_scale_f32_16x16x128_f8f6f4) vs "
+                      "k_grouped_gemm_bf16 on decoded MXFP4"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -317,6 +362,8 @@ def main():
     gu_ms = float(kern_ms[0])
 
     tail = tail_measurement(cfg, hip, sptr, min(K, 50))
+    w4a8 = (w4a8_measurement(dl, x, ids, hip, sptr, min(K, 20))
+            if cfg.wdtype == "mxfp4" and cfg.D % 128 == 0 and cfg.I % 128 == 0 else None)
 
     # algorithmic work of the gate/up SwiGLU GEMM launch (routed + shared groups)
     T, D, E, k, I, Is = cfg.T, cfg.D, cfg.E, cfg.k, cfg.I, cfg.I_shared
@@ -407,6 +454,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "tail": tail,
+        "w4a8": w4a8,
         "layer": {"alg_bytes": int(layer_bytes), "flops": int(layer_flops),
                   "gbs": round(layer_bytes / (ms_per_step * 1e-3) / 1e9, 1),
                   "hbm_frac": round(layer_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
