@@ -42,6 +42,8 @@ def parse():
     p.add_argument("--config", type=int, default=2, help="layer recipe (1..5), default 2")
     p.add_argument("--T", type=int, default=None, help="override the batch size")
     p.add_argument("--replicas", type=int, default=0, help="weight replicas (0 = auto)")
+    p.add_argument("--w4a8", action="store_true",
+                   help="MXFP4 routed experts on MXFP8 activations (FP4 x FP8 MFMA)")
     p.add_argument("--glu", choices=("swiglu", "clamp", "situ"), default="swiglu",
                    help="gated activation of the expert FFNs (clamped SwiGLU, SiTU-GLU)")
     p.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV",
@@ -282,6 +284,10 @@ def main():
     cfg = synth.CONFIGS[args.config]
     if args.T is not None:
         cfg = cfg.with_T(args.T)
+    if args.w4a8 and cfg.wdtype != "mxfp4":
+        print("bench.py: --w4a8 needs a recipe with MXFP4 routed weights (recipe 5)",
+              file=sys.stderr)
+        sys.exit(2)
     dev = "cuda:0"
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
@@ -295,7 +301,7 @@ def main():
         wbytes_routed += 3 * dl.gate_scale.numel()
     # replicas so the weights do not stay in the 256 MB last-level cache
     nrep = args.replicas or max(1, min(8, int(np.ceil(1.2e9 / max(wbytes_routed, 1)))))
-    layers = [sdev.layer_object(dl, args.glu)]
+    layers = [sdev.layer_object(dl, args.glu, args.w4a8)]
     for _ in range(nrep - 1):
         c = sdev.DeviceLayer(cfg, dl.w_router, dl.bias, dl.gate.clone(), dl.up.clone(),
                              dl.down.clone(),
@@ -305,7 +311,7 @@ def main():
                              None if dl.sh_gate is None else dl.sh_gate.clone(),
                              None if dl.sh_up is None else dl.sh_up.clone(),
                              None if dl.sh_down is None else dl.sh_down.clone())
-        layers.append(sdev.layer_object(c, args.glu))
+        layers.append(sdev.layer_object(c, args.glu, args.w4a8))
     x = sdev.x_device(cfg, dev)
     ids = sdev.token_ids_device(cfg, dev)
     y = torch.empty((cfg.T, cfg.D), dtype=x.dtype, device=dev)
@@ -384,7 +390,8 @@ def main():
                 "alg_bytes_per_launch": int(gu_bytes),
                 "avg_launch_ms": round(gu_ms, 5),
                 "mfma_tflops": round(gu_flops / (gu_ms * 1e-3) / 1e12, 2),
-                "mfma_frac": round(gu_flops / (gu_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+                "mfma_frac": round(gu_flops / (gu_ms * 1e-3) / 1e12 /
+                                   (FP8_PEAK_TFLOPS if args.w4a8 else BF16_PEAK_TFLOPS), 4)}
     if cfg.act == "f32":
         roofline["bound"] = "hbm"
 
@@ -445,9 +452,11 @@ def main():
         "config": {"workload": f"MoE layer recipe {cfg.cid} ({cfg.name}): T={T}, D={D}, E={E} "
                                f"routed + {1 if Is else 0} shared, top-{k} {cfg.route}, I={I}, "
                                f"I_shared={Is}, weights {cfg.wdtype}"
-                               + ("" if args.glu == "swiglu" else f", {args.glu} activation"),
+                               + ("" if args.glu == "swiglu" else f", {args.glu} activation")
+                               + (", MXFP8 activations (FP4 x FP8)" if args.w4a8 else ""),
                    "T": T, "D": D, "E": E, "k": k, "I": I, "I_shared": Is,
                    "routing": cfg.route, "weights": cfg.wdtype, "activation": args.glu,
+                   "activation_format": "mxfp8" if args.w4a8 else cfg.act,
                    "parallelism": "single GPU",
                    "weight_replicas": nrep, "experts_touched": U,
                    "max_rows_per_expert": int(counts.max())},

@@ -79,6 +79,12 @@ extern "C" {
  * Both bits together, or any other bit, give MOE_ERR_UNSUPPORTED. */
 #define MOE_FLAG_GLU_CLAMP 0x1u
 #define MOE_FLAG_GLU_SITU 0x2u
+/* moe_layer_forward only: the routed experts (MXFP4 weights) run FP4 x FP8,
+ * as moe_grouped_swiglu_w4a8 describes (x quantised to MXFP8 once per token,
+ * h per routed row); a shared expert must then be bf16 and keeps its bf16
+ * path.  Needs bf16 activations and D, I multiples of 128.
+ * moe_layer_workspace_bytes with w = MOE_MXFP4 covers this flag. */
+#define MOE_FLAG_W4A8 0x4u
 
 typedef enum {
   MOE_OK = 0,
@@ -288,7 +294,7 @@ int moe_combine_rmsnorm(const void* expert_out, const int32_t* topk_idx, const f
  *  routed: E experts; shared: NULL (no shared expert, I_shared ignored) or one
  *  expert with inter dim I_shared (bf16 when routed weights are MXFP4).
  *  flags: 0, MOE_FLAG_GLU_CLAMP or MOE_FLAG_GLU_SITU (the gated activation of
- *  the routed and the shared experts).
+ *  the routed and the shared experts), optionally | MOE_FLAG_W4A8.
  *  workspace: moe_layer_workspace_bytes(...) bytes.
  * ------------------------------------------------------------------------- */
 size_t moe_layer_workspace_bytes(int64_t T, int D, int E, int k, int I, int I_shared,

@@ -21,6 +21,7 @@ F32, BF16, MXFP4 = 0, 1, 2
 ROUTE = {"softmax": 0, "sigmoid": 1, "hash": 2}
 # flags values selecting the gated activation (MOE_FLAG_GLU_* in moe.h)
 GLU = {"swiglu": 0, "clamp": 0x1, "situ": 0x2}
+FLAG_W4A8 = 0x4  # moe_layer_forward: routed MXFP4 experts run FP4 x FP8
 STAGES = ("routing", "permute", "gate_up_gemm", "down_gemm", "combine")
 EXPORTS = ("moe_router_workspace_bytes", "moe_router_topk", "moe_routing_scores", "moe_permute_workspace_bytes",
            "moe_permute", "moe_grouped_swiglu_workspace_bytes", "moe_grouped_swiglu",
@@ -298,8 +299,9 @@ def layer_workspace_bytes(T, D, E, k, I, I_shared, act, wdtype) -> int:
 
 def layer_forward(x, token_ids, w_router, bias, routed: ExpertWeights,
                   shared: Optional[ExpertWeights], E: int, k: int, mode: str, out=None,
-                  workspace=None, stream=None, glu: str = "swiglu"):
-    """The whole layer: y [T, D].  glu: the gated activation of every expert FFN."""
+                  workspace=None, stream=None, glu: str = "swiglu", w4a8: bool = False):
+    """The whole layer: y [T, D].  glu: the gated activation of every expert FFN;
+    w4a8: routed MXFP4 experts on MXFP8 activations (FP4 x FP8 MFMA)."""
     T, D = x.shape
     I = routed.gate.shape[1]
     Is = shared.gate.shape[1] if shared is not None else 0
@@ -316,7 +318,8 @@ def layer_forward(x, token_ids, w_router, bias, routed: ExpertWeights,
     s = shared.as_struct() if shared is not None else None
     _check(L.moe_layer_forward(_ptr(x), _ptr(token_ids), _ptr(w_router), _ptr(bias),
                                ctypes.byref(r), ctypes.byref(s) if s is not None else None,
-                               T, D, E, k, I, Is, ROUTE[mode], act, GLU[glu], _ptr(out), ws_ptr,
+                               T, D, E, k, I, Is, ROUTE[mode], act,
+                               GLU[glu] | (FLAG_W4A8 if w4a8 else 0), _ptr(out), ws_ptr,
                                ws_bytes, _stream(stream)))
     return out
 
@@ -337,9 +340,9 @@ class MoELayer:
     """Device-resident layer weights plus a reusable workspace."""
 
     def __init__(self, w_router, bias, routed: ExpertWeights, shared: Optional[ExpertWeights],
-                 E: int, k: int, mode: str, glu: str = "swiglu"):
+                 E: int, k: int, mode: str, glu: str = "swiglu", w4a8: bool = False):
         self.w_router, self.bias, self.routed, self.shared = w_router, bias, routed, shared
-        self.E, self.k, self.mode, self.glu = E, k, mode, glu
+        self.E, self.k, self.mode, self.glu, self.w4a8 = E, k, mode, glu, w4a8
         self._ws = None
 
     def forward(self, x, token_ids=None, out=None, stream=None):
@@ -351,4 +354,4 @@ class MoELayer:
             self._ws = _workspace(nb, x.device)
         return layer_forward(x, token_ids, self.w_router, self.bias, self.routed, self.shared,
                              self.E, self.k, self.mode, out=out, workspace=self._ws,
-                             stream=stream, glu=self.glu)
+                             stream=stream, glu=self.glu, w4a8=self.w4a8)

@@ -101,13 +101,43 @@ int64_t layer_table_entries(int64_t T, int D, int E, int k, int I, int Is, moe_d
   return ffn_table_entries(T * k, T, D, E, I, Is, act);
 }
 
+// Plans of the layer's FFN when the routed experts run FP4 x FP8: the routed
+// GEMMs on the W4A8 kernel (64-row tiles), the bf16 shared expert on the bf16
+// kernel with 64-row tiles too, so one permutation launch writes all four
+// tile tables.
+struct W4a8Plans {
+  moe::GemmPlan up_r, up_s, dn_r, dn_s;
+  bool shared;
+};
+
+W4a8Plans w4a8_plans(int64_t R, int64_t T, int D, int E, int I, int Is) {
+  W4a8Plans p{};
+  p.up_r = moe::plan_w4a8_gemm({true, R, E, D, I, 2}, true);
+  p.dn_r = moe::plan_w4a8_gemm({true, R, E, I, D, 2}, false);
+  p.shared = Is > 0;
+  if (p.shared) {
+    const moe::SegShape su{false, T, 1, D, Is, 0}, sd{false, T, 1, Is, D, 0};
+    p.up_s = moe::plan_grouped_gemm(&su, 1, true, MOE_BF16, 64);  // 64-row tiles
+    p.dn_s = moe::plan_grouped_gemm(&sd, 1, false, MOE_BF16, 64);
+  }
+  return p;
+}
+
+int64_t w4a8_layer_entries(const W4a8Plans& p) {
+  int64_t n = moe::plan_table_entries(p.up_r) + moe::plan_table_entries(p.dn_r);
+  if (p.shared) n += moe::plan_table_entries(p.up_s) + moe::plan_table_entries(p.dn_s);
+  return n;
+}
+
 struct LayerLayout {
   size_t logits, idx, w, mask, wprefix, counts, offsets, row_token, pair_row, h, hs, o, s, tiles,
-      total;
+      xq, xsc, hq, hsc, total;
   int64_t tile_entries;
 };
 
-LayerLayout layer_layout(int64_t T, int D, int E, int k, int I, int Is, moe_dtype act) {
+// w4a8: also the MXFP8 copies of x and h (FP4 x FP8 routed experts).
+LayerLayout layer_layout(int64_t T, int D, int E, int k, int I, int Is, moe_dtype act,
+                         bool w4a8 = false) {
   const int64_t R = T * k, W = (T + 63) / 64;
   const size_t es = act_size(act);
   Carver c;
@@ -126,9 +156,48 @@ LayerLayout layer_layout(int64_t T, int D, int E, int k, int I, int Is, moe_dtyp
   L.o = c.take((size_t)R * D * es);
   L.s = c.take((size_t)T * (Is > 0 ? D : 0) * es);
   L.tile_entries = layer_table_entries(T, D, E, k, I, Is, act);
+  L.xq = L.xsc = L.hq = L.hsc = 0;
+  if (w4a8) {
+    const int64_t n = w4a8_layer_entries(w4a8_plans(R, T, D, E, I, Is));
+    if (n > L.tile_entries) L.tile_entries = n;
+  }
   L.tiles = c.take((size_t)L.tile_entries * sizeof(int4));
+  if (w4a8) {
+    L.xq = c.take((size_t)T * D);
+    L.xsc = c.take((size_t)T * (D / 32));
+    L.hq = c.take((size_t)R * I);
+    L.hsc = c.take((size_t)R * (I / 32));
+  }
   L.total = c.off;
   return L;
+}
+
+// The FP4 x FP8 layout is reserved for MXFP4 routed weights whenever the
+// shapes allow it, so a caller sizing for MXFP4 weights may set the flag.
+bool w4a8_shapes(int D, int I, moe_dtype act) {
+  return act == MOE_BF16 && D % 128 == 0 && I % 128 == 0;
+}
+
+// One FP4 x FP8 GEMM segment: A = E4M3 codes, AS = their scales.
+moe::GemmSeg w4a8_seg(const uint8_t* A, const uint8_t* AS, const int32_t* a_index,
+                      const int32_t* offsets, int64_t M, int G, int K, int N,
+                      const moe_expert_weights* w, bool gated, void* out) {
+  moe::GemmSeg g{};
+  g.A = A;
+  g.AS = AS;
+  g.a_index = a_index;
+  g.offsets = offsets;
+  g.M = M;
+  g.G = G;
+  g.K = K;
+  g.N = N;
+  g.W0 = gated ? w->gate : w->down;
+  g.W1 = gated ? w->up : nullptr;
+  g.S0 = gated ? w->gate_scale : w->down_scale;
+  g.S1 = gated ? w->up_scale : nullptr;
+  g.wfmt = 2;
+  g.out = out;
+  return g;
 }
 
 int check_dims(int64_t T, int D, int E, int k) {
@@ -448,36 +517,12 @@ int moe_grouped_swiglu_w4a8(const void* x_rows, const int32_t* row_index,
   moe::GemmArgs up{};
   up.nseg = 1;
   up.glu = glu;
-  moe::GemmSeg& a = up.seg[0];
-  a.A = xq;
-  a.AS = xs;
-  a.offsets = expert_offsets;
-  a.M = R;
-  a.G = E;
-  a.K = D;
-  a.N = I;
-  a.W0 = w->gate;
-  a.W1 = w->up;
-  a.S0 = w->gate_scale;
-  a.S1 = w->up_scale;
-  a.wfmt = 2;
-  a.out = h;
+  up.seg[0] = w4a8_seg(xq, xs, nullptr, expert_offsets, R, E, D, I, w, true, h);
   if (e == hipSuccess) e = moe::launch_grouped_gemm(pu, up, tiles_up, s);
   if (e == hipSuccess) e = moe::launch_mx_e4m3_quantize(h, nullptr, R, I, hq, hs, s);
   moe::GemmArgs dn{};
   dn.nseg = 1;
-  moe::GemmSeg& b = dn.seg[0];
-  b.A = hq;
-  b.AS = hs;
-  b.offsets = expert_offsets;
-  b.M = R;
-  b.G = E;
-  b.K = I;
-  b.N = D;
-  b.W0 = w->down;
-  b.S0 = w->down_scale;
-  b.wfmt = 2;
-  b.out = out;
+  dn.seg[0] = w4a8_seg(hq, hs, nullptr, expert_offsets, R, E, I, D, w, false, out);
   if (e == hipSuccess) e = moe::launch_grouped_gemm(pd, dn, tiles_dn, s);
   return hip_status(e, "grouped_swiglu_w4a8");
 }
@@ -544,9 +589,9 @@ int moe_combine_rmsnorm(const void* expert_out, const int32_t* topk_idx, const f
 
 size_t moe_layer_workspace_bytes(int64_t T, int D, int E, int k, int I, int I_shared,
                                  moe_dtype act, moe_dtype w) {
-  (void)w;
   if (T < 0 || D <= 0 || E <= 0 || k <= 0 || I <= 0) return 0;
-  return layer_layout(T, D, E, k, I, I_shared, act).total;
+  return layer_layout(T, D, E, k, I, I_shared, act, w == MOE_MXFP4 && w4a8_shapes(D, I, act))
+      .total;
 }
 
 int moe_layer_forward(const void* x, const int32_t* token_ids, const void* w_router,
@@ -558,7 +603,8 @@ int moe_layer_forward(const void* x, const int32_t* token_ids, const void* w_rou
   if ((rc = check_act(act))) return rc;
   if ((rc = check_dims(T, D, E, k))) return rc;
   int glu;
-  if ((rc = glu_from_flags(flags, &glu))) return rc;
+  const bool w4a8 = (flags & MOE_FLAG_W4A8) != 0;
+  if ((rc = glu_from_flags(flags & ~MOE_FLAG_W4A8, &glu))) return rc;
   if (I < 32 || I % 32) return fail(MOE_ERR_SHAPE, "I=%d must be a positive multiple of 32", I);
   if (mode != MOE_ROUTE_SOFTMAX && mode != MOE_ROUTE_SIGMOID && mode != MOE_ROUTE_HASH)
     return fail(MOE_ERR_SHAPE, "unknown routing mode %d", (int)mode);
@@ -578,7 +624,15 @@ int moe_layer_forward(const void* x, const int32_t* token_ids, const void* w_rou
     if (!aligned(w_router, 16)) return fail(MOE_ERR_ALIGN, "w_router must be 16-byte aligned");
     if (bias && !aligned(bias, 4)) return fail(MOE_ERR_ALIGN, "bias misaligned");
   }
-  const LayerLayout L = layer_layout(T, D, E, k, I, Is, act);
+  if (w4a8) {
+    if (!routed || routed->dtype != MOE_MXFP4)
+      return fail(MOE_ERR_DTYPE, "MOE_FLAG_W4A8 needs MXFP4 routed weights");
+    if (!w4a8_shapes(D, I, act))
+      return fail(MOE_ERR_SHAPE, "MOE_FLAG_W4A8 needs bf16 activations and D, I multiples of 128");
+    if (shared && shared->dtype != MOE_BF16)
+      return fail(MOE_ERR_UNSUPPORTED, "MOE_FLAG_W4A8 runs a bf16 shared expert only");
+  }
+  const LayerLayout L = layer_layout(T, D, E, k, I, Is, act, w4a8);
   if (!workspace || workspace_bytes < L.total)
     return fail(MOE_ERR_WORKSPACE, "layer workspace needs %zu bytes", L.total);
   if (!aligned(workspace, 256)) return fail(MOE_ERR_ALIGN, "workspace must be 256-byte aligned");
@@ -601,16 +655,36 @@ int moe_layer_forward(const void* x, const int32_t* token_ids, const void* w_rou
   void* sh = ws + L.s;
   const int64_t R = T * k;
 
-  const FfnPlans p = ffn_plans(R, T, D, E, I, Is, act, routed->dtype == MOE_MXFP4 ? 1 : 0,
-                               shared && shared->dtype == MOE_MXFP4 ? 1 : 0);
-  if (!p.up.valid || !p.dn.valid) return fail(MOE_ERR_SHAPE, "problem too large for one launch");
-  if (moe::plan_table_entries(p.up) + moe::plan_table_entries(p.dn) > L.tile_entries)
-    return fail(MOE_ERR_WORKSPACE, "tile tables exceed their workspace region");
-  int4* tiles_up = reinterpret_cast<int4*>(ws + L.tiles);
-  int4* tiles_dn = tiles_up + moe::plan_table_entries(p.up);
+  // Tile plans; the permutation launch writes their tables.
+  int4* tiles = reinterpret_cast<int4*>(ws + L.tiles);
   moe::TileJobs jobs{};
-  if (!moe::plan_tile_jobs(p.up, tiles_up, jobs) || !moe::plan_tile_jobs(p.dn, tiles_dn, jobs))
-    return fail(MOE_ERR_UNSUPPORTED, "gate/up and down GEMM plans use different row tiles");
+  FfnPlans p{};
+  W4a8Plans q{};
+  int4 *tiles_up = tiles, *tiles_dn = nullptr, *tiles_up_s = nullptr, *tiles_dn_s = nullptr;
+  if (!w4a8) {
+    p = ffn_plans(R, T, D, E, I, Is, act, routed->dtype == MOE_MXFP4 ? 1 : 0,
+                  shared && shared->dtype == MOE_MXFP4 ? 1 : 0);
+    if (!p.up.valid || !p.dn.valid) return fail(MOE_ERR_SHAPE, "problem too large for one launch");
+    if (moe::plan_table_entries(p.up) + moe::plan_table_entries(p.dn) > L.tile_entries)
+      return fail(MOE_ERR_WORKSPACE, "tile tables exceed their workspace region");
+    tiles_dn = tiles_up + moe::plan_table_entries(p.up);
+    if (!moe::plan_tile_jobs(p.up, tiles_up, jobs) || !moe::plan_tile_jobs(p.dn, tiles_dn, jobs))
+      return fail(MOE_ERR_UNSUPPORTED, "gate/up and down GEMM plans use different row tiles");
+  } else {
+    q = w4a8_plans(R, T, D, E, I, Is);
+    if (!q.up_r.valid || !q.dn_r.valid || (shared && (!q.up_s.valid || !q.dn_s.valid)))
+      return fail(MOE_ERR_SHAPE, "problem too large for one launch");
+    if (w4a8_layer_entries(q) > L.tile_entries)
+      return fail(MOE_ERR_WORKSPACE, "tile tables exceed their workspace region");
+    tiles_up_s = tiles_up + moe::plan_table_entries(q.up_r);
+    tiles_dn = tiles_up_s + (shared ? moe::plan_table_entries(q.up_s) : 0);
+    tiles_dn_s = tiles_dn + moe::plan_table_entries(q.dn_r);
+    if (!moe::plan_tile_jobs(q.up_r, tiles_up, jobs) ||
+        (shared && !moe::plan_tile_jobs(q.up_s, tiles_up_s, jobs)) ||
+        !moe::plan_tile_jobs(q.dn_r, tiles_dn, jobs) ||
+        (shared && !moe::plan_tile_jobs(q.dn_s, tiles_dn_s, jobs)))
+      return fail(MOE_ERR_UNSUPPORTED, "the FFN plans use different row tiles");
+  }
 
   record_stage(0, s);
   hipError_t e;
@@ -627,28 +701,70 @@ int moe_layer_forward(const void* x, const int32_t* token_ids, const void* w_rou
   if (e != hipSuccess) return hip_status(e, "permute");
   record_stage(2, s);
 
-  moe::GemmArgs up{};
-  up.seg[0] = make_seg(x, row_token, offsets, R, E, D, I, routed, true, h);
-  up.nseg = 1;
-  up.glu = glu;
-  if (shared) {
-    up.seg[1] = make_seg(x, nullptr, nullptr, T, 1, D, Is, shared, true, hs);
-    up.nseg = 2;
+  if (!w4a8) {
+    moe::GemmArgs up{};
+    up.seg[0] = make_seg(x, row_token, offsets, R, E, D, I, routed, true, h);
+    up.nseg = 1;
+    up.glu = glu;
+    if (shared) {
+      up.seg[1] = make_seg(x, nullptr, nullptr, T, 1, D, Is, shared, true, hs);
+      up.nseg = 2;
+    }
+    e = moe::launch_grouped_gemm(p.up, up, tiles_up, s, kernel_event(MOE_STAGE_EVENTS),
+                                 kernel_event(MOE_STAGE_EVENTS + 1));
+  } else {
+    // x quantised once per token; the routed GEMM gathers codes and scales
+    // through row_token
+    uint8_t* xq = reinterpret_cast<uint8_t*>(ws + L.xq);
+    uint8_t* xsc = reinterpret_cast<uint8_t*>(ws + L.xsc);
+    e = moe::launch_mx_e4m3_quantize(x, nullptr, T, D, xq, xsc, s);
+    moe::GemmArgs up{};
+    up.seg[0] = w4a8_seg(xq, xsc, row_token, offsets, R, E, D, I, routed, true, h);
+    up.nseg = 1;
+    up.glu = glu;
+    if (e == hipSuccess)
+      e = moe::launch_grouped_gemm(q.up_r, up, tiles_up, s, kernel_event(MOE_STAGE_EVENTS),
+                                   shared ? nullptr : kernel_event(MOE_STAGE_EVENTS + 1));
+    if (e == hipSuccess && shared) {
+      moe::GemmArgs us{};
+      us.seg[0] = make_seg(x, nullptr, nullptr, T, 1, D, Is, shared, true, hs);
+      us.nseg = 1;
+      us.glu = glu;
+      e = moe::launch_grouped_gemm(q.up_s, us, tiles_up_s, s, nullptr,
+                                   kernel_event(MOE_STAGE_EVENTS + 1));
+    }
   }
-  e = moe::launch_grouped_gemm(p.up, up, tiles_up, s, kernel_event(MOE_STAGE_EVENTS),
-                               kernel_event(MOE_STAGE_EVENTS + 1));
   if (e != hipSuccess) return hip_status(e, "gate/up GEMM");
   record_stage(3, s);
 
-  moe::GemmArgs dn{};
-  dn.seg[0] = make_seg(h, nullptr, offsets, R, E, I, D, routed, false, o);
-  dn.nseg = 1;
-  if (shared) {
-    dn.seg[1] = make_seg(hs, nullptr, nullptr, T, 1, Is, D, shared, false, sh);
-    dn.nseg = 2;
+  if (!w4a8) {
+    moe::GemmArgs dn{};
+    dn.seg[0] = make_seg(h, nullptr, offsets, R, E, I, D, routed, false, o);
+    dn.nseg = 1;
+    if (shared) {
+      dn.seg[1] = make_seg(hs, nullptr, nullptr, T, 1, Is, D, shared, false, sh);
+      dn.nseg = 2;
+    }
+    e = moe::launch_grouped_gemm(p.dn, dn, tiles_dn, s, kernel_event(MOE_STAGE_EVENTS + 2),
+                                 kernel_event(MOE_STAGE_EVENTS + 3));
+  } else {
+    uint8_t* hq = reinterpret_cast<uint8_t*>(ws + L.hq);
+    uint8_t* hsc = reinterpret_cast<uint8_t*>(ws + L.hsc);
+    e = moe::launch_mx_e4m3_quantize(h, nullptr, R, I, hq, hsc, s);
+    moe::GemmArgs dn{};
+    dn.seg[0] = w4a8_seg(hq, hsc, nullptr, offsets, R, E, I, D, routed, false, o);
+    dn.nseg = 1;
+    if (e == hipSuccess)
+      e = moe::launch_grouped_gemm(q.dn_r, dn, tiles_dn, s, kernel_event(MOE_STAGE_EVENTS + 2),
+                                   shared ? nullptr : kernel_event(MOE_STAGE_EVENTS + 3));
+    if (e == hipSuccess && shared) {
+      moe::GemmArgs ds{};
+      ds.seg[0] = make_seg(hs, nullptr, nullptr, T, 1, Is, D, shared, false, sh);
+      ds.nseg = 1;
+      e = moe::launch_grouped_gemm(q.dn_s, ds, tiles_dn_s, s, nullptr,
+                                   kernel_event(MOE_STAGE_EVENTS + 3));
+    }
   }
-  e = moe::launch_grouped_gemm(p.dn, dn, tiles_dn, s, kernel_event(MOE_STAGE_EVENTS + 2),
-                               kernel_event(MOE_STAGE_EVENTS + 3));
   if (e != hipSuccess) return hip_status(e, "down GEMM");
   record_stage(4, s);
 

@@ -93,15 +93,16 @@ def upload_layer(cfg: synth.LayerConfig, device="cuda") -> DeviceLayer:
     return DeviceLayer(cfg, wr, bias, gate, up, down, gs, us, ds, shg, shu, shd)
 
 
-def layer_object(dl: DeviceLayer, glu: str = "swiglu"):
-    """The binding's MoELayer over uploaded weights (glu: the experts' gated activation)."""
+def layer_object(dl: DeviceLayer, glu: str = "swiglu", w4a8: bool = False):
+    """The binding's MoELayer over uploaded weights (glu: the experts' gated activation;
+    w4a8: MXFP4 routed experts on MXFP8 activations)."""
     import invariant_moe_amd as moe
     routed = moe.ExpertWeights(dl.gate, dl.up, dl.down, dl.gate_scale, dl.up_scale, dl.down_scale)
     shared = None
     if dl.sh_gate is not None:
         shared = moe.ExpertWeights(dl.sh_gate, dl.sh_up, dl.sh_down)
     return moe.MoELayer(dl.w_router, dl.bias, routed, shared, dl.cfg.E, dl.cfg.k, dl.cfg.route,
-                        glu=glu)
+                        glu=glu, w4a8=w4a8)
 
 
 def x_device(cfg: synth.LayerConfig, device="cuda", T=None, offset_tokens=0) -> torch.Tensor:

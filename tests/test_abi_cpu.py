@@ -85,7 +85,7 @@ def _layer(**kw):
     (dict(wsb=16), -5),
     (dict(ws=None), -5),
     (dict(flags=3), -6),         # both gated activations
-    (dict(flags=4), -6),         # unknown flag bit
+    (dict(flags=8), -6),         # unknown flag bit
     (dict(flags=0x80000001), -6),
     (dict(mode=2), -1),          # hash without token ids
     (dict(mode=7), -2),
@@ -151,3 +151,24 @@ def test_norm_entry_points_reject():
     assert L.moe_combine_rmsnorm(f, f, f, f, _fake(0x100004), f, f, 1e-6, 4, 2, 64, 1, f, f,
                                  None) == -4
     assert L.moe_combine_rmsnorm(f, f, f, f, None, f, f, -0.5, 4, 2, 64, 1, f, f, None) == -6
+
+
+def test_w4a8_layer_flag_rejects():
+    # bf16 routed weights, MXFP4 without multiples of 128, an MXFP4 shared expert
+    assert _layer(flags=4)[0] == -3
+    assert _layer(flags=4, routed=_weights(dtype=2, scales=True), D=288)[0] == -2
+    assert _layer(flags=4, routed=_weights(dtype=2, scales=True), D=256, I=128,
+                  shared=_weights(dtype=2, scales=True), Is=128)[0] == -6
+    assert _layer(flags=8)[0] == -6  # unknown bit
+    L = moe.lib()
+    w = _weights()
+    # the grouped entry points take no W4A8 bit; the W4A8 one needs MXFP4 weights
+    assert L.moe_grouped_swiglu(_fake(), None, _fake(), 10, 4, 128, 128, ctypes.byref(w), 1, 4,
+                                _fake(), _fake(), 1 << 20, None) == -6
+    assert L.moe_grouped_swiglu_w4a8(_fake(), None, _fake(), 10, 4, 128, 128, ctypes.byref(w), 0,
+                                      _fake(), _fake(), 1 << 20, None) == -3
+    assert L.moe_grouped_swiglu_w4a8(_fake(), None, _fake(), 10, 4, 160, 128, ctypes.byref(w), 0,
+                                      _fake(), _fake(), 1 << 20, None) == -2
+    # the workspace query with MXFP4 weights covers the flag
+    assert L.moe_layer_workspace_bytes(2048, 7168, 256, 8, 2048, 2048, 1, 2) > \
+        L.moe_layer_workspace_bytes(2048, 7168, 256, 8, 2048, 2048, 1, 1)

@@ -112,3 +112,38 @@ def test_grouped_ffn_w4a8_rows_equal_in_any_batch():
         got = to_np(moe.grouped_swiglu_w4a8(dev(x), dev(sub_rows.astype(np.int32)), dev(sub_off),
                                             len(sub_rows), E, w))
         assert np.array_equal(got, full[sub_rows]), keep
+
+
+def test_layer_w4a8_vs_composed_oracle_and_invariance():
+    """moe_layer_forward with MOE_FLAG_W4A8: routing, the FP4 x FP8 routed
+    experts, the bf16 shared expert and the combine, against the oracle's
+    stages composed; a token's row is the same bits at every T."""
+    banner("w4a8 layer")
+    E, k, D, I, Is, T = 8, 2, 256, 128, 128, 150
+    m = _experts(97, E, D, I)
+    sh = [synth.normal_bf16(98, t, n, 0.05).reshape(shape)
+          for t, (n, shape) in enumerate(((Is * D, (Is, D)), (Is * D, (Is, D)), (D * Is, (D, Is))))]
+    wr = synth.normal_bf16(99, 0, E * D, 0.05).reshape(E, D)
+    x = synth.normal_bf16(100, 0, T * D, 1.0).reshape(T, D)
+    routed = moe.ExpertWeights(*(dev(a[0]) for a in m), *(dev(a[1]) for a in m))
+    shared = moe.ExpertWeights(*(dev(a[None]) for a in sh))
+    layer = moe.MoELayer(dev(wr), None, routed, shared, E, k, "softmax", w4a8=True)
+    y = to_np(layer.forward(dev(x)))
+    idx, w = oracle.route(oracle.router_logits(x, wr), None, None, T, E, k, "softmax")
+    _, offsets, row_token, pair_row = oracle.permute(idx, E)
+    o_ref = np.empty((T * k, D), np.uint16)
+    for e in range(E):
+        a, b = offsets[e], offsets[e + 1]
+        if b > a:
+            o_ref[a:b] = oracle.expert_ffn_w4a8(np.ascontiguousarray(x[row_token[a:b]]),
+                                                *[(a_[0][e], a_[1][e]) for a_ in m])
+    s_ref = oracle.expert_ffn(x, *sh, "bf16")
+    y_ref = oracle.combine(o_ref, idx, w, pair_row, s_ref, T, k, D)
+    r = rel_l2(y, y_ref)
+    banner(f"w4a8 layer rel_l2={r:.3e}")
+    assert r <= 2e-3, r
+    # not the W4A16 layer: the activations were quantised
+    plain = to_np(moe.MoELayer(dev(wr), None, routed, shared, E, k, "softmax").forward(dev(x)))
+    assert not np.array_equal(plain, y)
+    for t in (37, 5, 1):
+        assert np.array_equal(to_np(layer.forward(dev(np.ascontiguousarray(x[:t])))), y[:t]), t
