@@ -3,6 +3,7 @@
 // include/moe.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -112,13 +113,15 @@ struct W4a8Plans {
 
 W4a8Plans w4a8_plans(int64_t R, int64_t T, int D, int E, int I, int Is) {
   W4a8Plans p{};
-  p.up_r = moe::plan_w4a8_gemm({true, R, E, D, I, 2}, true);
-  p.dn_r = moe::plan_w4a8_gemm({true, R, E, I, D, 2}, false);
+  const int64_t hint = R / E;
+  p.up_r = moe::plan_w4a8_gemm({true, R, E, D, I, 2}, true, hint);
+  p.dn_r = moe::plan_w4a8_gemm({true, R, E, I, D, 2}, false, hint);
   p.shared = Is > 0;
-  if (p.shared) {
+  if (p.shared) {  // the bf16 planner's tile for the same hint has the same row tile
     const moe::SegShape su{false, T, 1, D, Is, 0}, sd{false, T, 1, Is, D, 0};
-    p.up_s = moe::plan_grouped_gemm(&su, 1, true, MOE_BF16, 64);  // 64-row tiles
-    p.dn_s = moe::plan_grouped_gemm(&sd, 1, false, MOE_BF16, 64);
+    const int64_t sh = p.up_r.l[0].BM == 128 ? 128 : 64;
+    p.up_s = moe::plan_grouped_gemm(&su, 1, true, MOE_BF16, sh);
+    p.dn_s = moe::plan_grouped_gemm(&sd, 1, false, MOE_BF16, sh);
   }
   return p;
 }
@@ -459,8 +462,11 @@ int moe_mx_e4m3_quantize(const void* x, const int32_t* row_index, int64_t R, int
 // x codes + scales, h (bf16), h codes + scales, then the two GEMMs' tile tables.
 static int64_t w4a8_table_entries(int64_t R, int E, int D, int I) {
   moe::SegShape up{true, R, E, D, I, 2}, dn{true, R, E, I, D, 2};
-  return moe::plan_table_entries(moe::plan_w4a8_gemm(up, true)) +
-         moe::plan_table_entries(moe::plan_w4a8_gemm(dn, false));
+  int64_t n = 0;
+  for (int64_t hint : {(int64_t)0, (int64_t)1 << 30})  // either row tile
+    n = std::max(n, moe::plan_table_entries(moe::plan_w4a8_gemm(up, true, hint)) +
+                        moe::plan_table_entries(moe::plan_w4a8_gemm(dn, false, hint)));
+  return n;
 }
 
 size_t moe_grouped_swiglu_w4a8_workspace_bytes(int64_t R, int E, int D, int I) {
@@ -498,7 +504,8 @@ int moe_grouped_swiglu_w4a8(const void* x_rows, const int32_t* row_index,
   if (R == 0) return ok();
   hipStream_t s = static_cast<hipStream_t>(stream);
   moe::SegShape su{true, R, E, D, I, 2}, sd{true, R, E, I, D, 2};
-  const moe::GemmPlan pu = moe::plan_w4a8_gemm(su, true), pd = moe::plan_w4a8_gemm(sd, false);
+  const moe::GemmPlan pu = moe::plan_w4a8_gemm(su, true, R / E),
+                      pd = moe::plan_w4a8_gemm(sd, false, R / E);
   if (!pu.valid || !pd.valid) return fail(MOE_ERR_SHAPE, "problem too large for one launch");
   char* ws = static_cast<char*>(workspace);
   Carver c;

@@ -554,8 +554,8 @@ __device__ __forceinline__ int lds_line_off(int line, int chunk) {
   return line * 128 + ((chunk ^ (line & 7)) << 4);
 }
 
-template <int BM, int BN, int WM, int WN, bool GATED>
-__global__ __launch_bounds__(64 * WM * WN, 2) void k_grouped_gemm_w4a8(GemmArgs args) {
+template <int BM, int BN, int WM, int WN, bool GATED, int MINW>
+__global__ __launch_bounds__(64 * WM * WN, MINW) void k_grouped_gemm_w4a8(GemmArgs args) {
   constexpr int NT = 64 * WM * WN;
   constexpr int NMAT = GATED ? 2 : 1;
   constexpr int TBW = BM / 16 / WM;
@@ -750,7 +750,8 @@ enum TileCfg {
   TILE_128x128_2x4_P2,    // prefill gate/up: 8 waves, two per SIMD
   TILE_COUNT,
   TILE_F32 = 100,         // fp32 VALU kernel, 16 x 16 tiles
-  TILE_W4A8 = 200         // FP4 x FP8 kernel, 64 x 64 tiles on 2 x 2 waves
+  TILE_W4A8 = 200,        // FP4 x FP8 kernel, 64 x 64 tiles on 2 x 2 waves
+  TILE_W4A8_128 = 201     // FP4 x FP8 kernel, 128 x 128 tiles on 2 x 4 waves
 };
 
 struct TileShape {
@@ -768,6 +769,7 @@ static TileShape tile_shape(int cfg) {
     case TILE_128x128_2x2_P2: return {128, 128};
     case TILE_128x128_2x4_P2: return {128, 128};
     case TILE_W4A8: return {64, 64};
+    case TILE_W4A8_128: return {128, 128};
     default: return {16, 16};  // TILE_F32
   }
 }
@@ -859,7 +861,7 @@ GemmPlan plan_grouped_gemm(const SegShape* segs, int nseg, bool gated, int act,
   return p;
 }
 
-GemmPlan plan_w4a8_gemm(const SegShape& seg, bool gated) {
+GemmPlan plan_w4a8_gemm(const SegShape& seg, bool gated, int64_t rows_per_group_hint) {
   GemmPlan p{};
   p.valid = true;
   p.gated = gated;
@@ -868,10 +870,11 @@ GemmPlan plan_w4a8_gemm(const SegShape& seg, bool gated) {
   p.seg[0] = seg;
   PlanLaunch& L = p.l[0];
   L.seg_mask = 1;
-  L.cfg = TILE_W4A8;
-  L.BM = 64;
-  L.BN = 64;
-  L.grid = (seg_tile_bound(seg, 64, 64) + 7) / 8 * 8;
+  L.cfg = rows_per_group_hint > 96 ? TILE_W4A8_128 : TILE_W4A8;
+  const TileShape ts = tile_shape(L.cfg);
+  L.BM = ts.BM;
+  L.BN = ts.BN;
+  L.grid = (seg_tile_bound(seg, ts.BM, ts.BN) + 7) / 8 * 8;
   if (L.grid > 0x7ffffff8) p.valid = false;
   if (L.grid > 0) p.n = 1;
   return p;
@@ -917,13 +920,20 @@ hipError_t launch_grouped_gemm(const GemmPlan& p, const GemmArgs& a, int4* table
     one.glu = a.glu;
     const LaunchEvents ev{i == 0 ? ev_start : nullptr, i == p.n - 1 ? ev_stop : nullptr};
     hipError_t e;
-    if (L.cfg == TILE_W4A8) {
-      if (p.gated)
-        hipExtLaunchKernelGGL((k_grouped_gemm_w4a8<64, 64, 2, 2, true>), dim3((unsigned)L.grid),
-                              dim3(256), 0, st, ev.start, ev.stop, 0, one);
+    if (L.cfg == TILE_W4A8 || L.cfg == TILE_W4A8_128) {
+      const dim3 g((unsigned)L.grid);
+      if (L.cfg == TILE_W4A8 && p.gated)
+        hipExtLaunchKernelGGL((k_grouped_gemm_w4a8<64, 64, 2, 2, true, 2>), g, dim3(256), 0, st,
+                              ev.start, ev.stop, 0, one);
+      else if (L.cfg == TILE_W4A8)
+        hipExtLaunchKernelGGL((k_grouped_gemm_w4a8<64, 64, 2, 2, false, 2>), g, dim3(256), 0, st,
+                              ev.start, ev.stop, 0, one);
+      else if (p.gated)
+        hipExtLaunchKernelGGL((k_grouped_gemm_w4a8<128, 128, 2, 4, true, 1>), g, dim3(512), 0, st,
+                              ev.start, ev.stop, 0, one);
       else
-        hipExtLaunchKernelGGL((k_grouped_gemm_w4a8<64, 64, 2, 2, false>), dim3((unsigned)L.grid),
-                              dim3(256), 0, st, ev.start, ev.stop, 0, one);
+        hipExtLaunchKernelGGL((k_grouped_gemm_w4a8<128, 128, 2, 4, false, 1>), g, dim3(512), 0, st,
+                              ev.start, ev.stop, 0, one);
       e = hipGetLastError();
     } else if (L.cfg == TILE_F32) {
       if (p.gated)

@@ -98,6 +98,7 @@ def test_grouped_ffn_w4a8_vs_oracle(glu):
 
 
 def test_grouped_ffn_w4a8_rows_equal_in_any_batch():
+    """100 rows per expert take 128-row tiles, the smaller batches 64-row tiles."""
     banner("w4a8 batch invariance")
     E, D, I = 4, 256, 128
     m = _experts(95, E, D, I)
@@ -117,9 +118,10 @@ def test_grouped_ffn_w4a8_rows_equal_in_any_batch():
 def test_layer_w4a8_vs_composed_oracle_and_invariance():
     """moe_layer_forward with MOE_FLAG_W4A8: routing, the FP4 x FP8 routed
     experts, the bf16 shared expert and the combine, against the oracle's
-    stages composed; a token's row is the same bits at every T."""
+    stages composed; a token's row is the same bits at every T, across the
+    128-row and 64-row tiles (routed FP4 x FP8 and shared bf16 alike)."""
     banner("w4a8 layer")
-    E, k, D, I, Is, T = 8, 2, 256, 128, 128, 150
+    E, k, D, I, Is, T = 8, 2, 256, 128, 128, 400  # 100 rows per expert: 128-row tiles
     m = _experts(97, E, D, I)
     sh = [synth.normal_bf16(98, t, n, 0.05).reshape(shape)
           for t, (n, shape) in enumerate(((Is * D, (Is, D)), (Is * D, (Is, D)), (D * Is, (D, Is))))]
@@ -145,5 +147,5 @@ def test_layer_w4a8_vs_composed_oracle_and_invariance():
     # not the W4A16 layer: the activations were quantised
     plain = to_np(moe.MoELayer(dev(wr), None, routed, shared, E, k, "softmax").forward(dev(x)))
     assert not np.array_equal(plain, y)
-    for t in (37, 5, 1):
+    for t in (150, 37, 5, 1):  # 64-row tiles
         assert np.array_equal(to_np(layer.forward(dev(np.ascontiguousarray(x[:t])))), y[:t]), t
