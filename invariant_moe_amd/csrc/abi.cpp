@@ -463,7 +463,7 @@ int moe_mx_e4m3_quantize(const void* x, const int32_t* row_index, int64_t R, int
 static int64_t w4a8_table_entries(int64_t R, int E, int D, int I) {
   moe::SegShape up{true, R, E, D, I, 2}, dn{true, R, E, I, D, 2};
   int64_t n = 0;
-  for (int64_t hint : {(int64_t)0, (int64_t)1 << 30})  // either row tile
+  for (int64_t hint : {(int64_t)0, (int64_t)64, (int64_t)1 << 30})  // every tile shape
     n = std::max(n, moe::plan_table_entries(moe::plan_w4a8_gemm(up, true, hint)) +
                         moe::plan_table_entries(moe::plan_w4a8_gemm(dn, false, hint)));
   return n;

@@ -597,16 +597,23 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_grouped_gemm_w4a8(GemmAr
     const uint8_t* base = static_cast<const uint8_t*>(mat ? s.W1 : s.W0);
     wsrc[i] = base + ((int64_t)ti.g * N + nn) * (K / 2) + (c % 4) * 16;
   }
-  // scale words (the 4 E8M0 bytes of one row's stage): tokens by threads
-  // 0..BM-1, weight rows by threads BM..BM+NMAT*BN-1
-  const uint8_t* scsrc = nullptr;
-  if (tid < BM) {
-    int64_t row = ti.row0 + min(tid, ti.rows - 1);
-    if (s.a_index) row = s.a_index[row];
-    scsrc = s.AS + row * (K / 32);
-  } else if (tid < BM + NMAT * BN) {
-    const int c = tid - BM, mat = c / BN, nn = min(ti.n0 + c % BN, N - 1);
-    scsrc = (mat ? s.S1 : s.S0) + ((int64_t)ti.g * N + nn) * (K / 32);
+  // scale words (the 4 E8M0 bytes of one row's stage): word w < BM is token
+  // row w, word BM + c weight row c; thread t takes words t + i * NT (words
+  // past the end read token row 0's word and are not stored)
+  constexpr int SW = BM + NMAT * BN;
+  constexpr int SPT = (SW + NT - 1) / NT;
+  const uint8_t* scsrc[SPT];
+#pragma unroll
+  for (int i = 0; i < SPT; ++i) {
+    const int w = tid + i * NT;
+    if (w >= BM && w < SW) {
+      const int c = w - BM, mat = c / BN, nn = min(ti.n0 + c % BN, N - 1);
+      scsrc[i] = (mat ? s.S1 : s.S0) + ((int64_t)ti.g * N + nn) * (K / 32);
+    } else {
+      int64_t row = ti.row0 + (w < BM ? min(w, ti.rows - 1) : 0);
+      if (s.a_index) row = s.a_index[row];
+      scsrc[i] = s.AS + row * (K / 32);
+    }
   }
 
   f32x4_t acc[NMAT][NBW][TBW];
@@ -619,17 +626,19 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_grouped_gemm_w4a8(GemmAr
 
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // native: plain loads and stores
   u32x4 xr[XPT], wr[WPT];
-  uint32_t sc = 127u;
+  uint32_t sc[SPT];
   // stage loads into registers, then into LDS (the arrays are passed, not
   // captured, so that they stay in registers)
-  auto gload = [&](u32x4 (&xq)[XPT], u32x4 (&wq)[WPT], uint32_t& scq, int kt) {
+  auto gload = [&](u32x4 (&xq)[XPT], u32x4 (&wq)[WPT], uint32_t (&scq)[SPT], int kt) {
 #pragma unroll
     for (int i = 0; i < XPT; ++i) xq[i] = *reinterpret_cast<const u32x4*>(xsrc[i] + kt * KQ);
 #pragma unroll
     for (int i = 0; i < WPT; ++i) wq[i] = *reinterpret_cast<const u32x4*>(wsrc[i] + kt * (KQ / 2));
-    if (scsrc) scq = *reinterpret_cast<const uint32_t*>(scsrc + kt * 4);
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) scq[i] = *reinterpret_cast<const uint32_t*>(scsrc[i] + kt * 4);
   };
-  auto lstore = [&](const u32x4 (&xq)[XPT], const u32x4 (&wq)[WPT], uint32_t scq, int buf) {
+  auto lstore = [&](const u32x4 (&xq)[XPT], const u32x4 (&wq)[WPT], const uint32_t (&scq)[SPT],
+                    int buf) {
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
       const int c = tid + i * NT;
@@ -645,10 +654,14 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_grouped_gemm_w4a8(GemmAr
             wq[i];
       }
     }
-    if (tid < BM)
-      ssx[buf][tid] = scq;
-    else if (tid < BM + NMAT * BN)
-      ssw[buf][tid - BM] = scq;
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+      const int w = tid + i * NT;
+      if (w < BM)
+        ssx[buf][w] = scq[i];
+      else if (w < SW)
+        ssw[buf][w - BM] = scq[i];
+    }
   };
   const int g4 = lane >> 4, r16 = lane & 15;
   auto compute = [&](int buf) {
@@ -751,7 +764,8 @@ enum TileCfg {
   TILE_COUNT,
   TILE_F32 = 100,         // fp32 VALU kernel, 16 x 16 tiles
   TILE_W4A8 = 200,        // FP4 x FP8 kernel, 64 x 64 tiles on 2 x 2 waves
-  TILE_W4A8_128 = 201     // FP4 x FP8 kernel, 128 x 128 tiles on 2 x 4 waves
+  TILE_W4A8_N128 = 201,   // FP4 x FP8 kernel, 64 x 128 tiles on 2 x 2 waves
+  TILE_W4A8_128 = 202     // FP4 x FP8 kernel, 128 x 128 tiles on 2 x 4 waves
 };
 
 struct TileShape {
@@ -769,6 +783,7 @@ static TileShape tile_shape(int cfg) {
     case TILE_128x128_2x2_P2: return {128, 128};
     case TILE_128x128_2x4_P2: return {128, 128};
     case TILE_W4A8: return {64, 64};
+    case TILE_W4A8_N128: return {64, 128};
     case TILE_W4A8_128: return {128, 128};
     default: return {16, 16};  // TILE_F32
   }
@@ -870,7 +885,12 @@ GemmPlan plan_w4a8_gemm(const SegShape& seg, bool gated, int64_t rows_per_group_
   p.seg[0] = seg;
   PlanLaunch& L = p.l[0];
   L.seg_mask = 1;
-  L.cfg = rows_per_group_hint > 96 ? TILE_W4A8_128 : TILE_W4A8;
+  // Measured at D=7168, I=2048: 64 x 64 is the fastest at 8 rows per expert
+  // (most workgroups for the weight stream), 64 x 128 at 64 rows (half the
+  // token re-reads, -12 %), 128 x 128 at 256 rows.
+  L.cfg = rows_per_group_hint > 96   ? TILE_W4A8_128
+          : rows_per_group_hint > 16 ? TILE_W4A8_N128
+                                     : TILE_W4A8;
   const TileShape ts = tile_shape(L.cfg);
   L.BM = ts.BM;
   L.BN = ts.BN;
@@ -920,13 +940,19 @@ hipError_t launch_grouped_gemm(const GemmPlan& p, const GemmArgs& a, int4* table
     one.glu = a.glu;
     const LaunchEvents ev{i == 0 ? ev_start : nullptr, i == p.n - 1 ? ev_stop : nullptr};
     hipError_t e;
-    if (L.cfg == TILE_W4A8 || L.cfg == TILE_W4A8_128) {
+    if (L.cfg == TILE_W4A8 || L.cfg == TILE_W4A8_N128 || L.cfg == TILE_W4A8_128) {
       const dim3 g((unsigned)L.grid);
       if (L.cfg == TILE_W4A8 && p.gated)
         hipExtLaunchKernelGGL((k_grouped_gemm_w4a8<64, 64, 2, 2, true, 2>), g, dim3(256), 0, st,
                               ev.start, ev.stop, 0, one);
       else if (L.cfg == TILE_W4A8)
         hipExtLaunchKernelGGL((k_grouped_gemm_w4a8<64, 64, 2, 2, false, 2>), g, dim3(256), 0, st,
+                              ev.start, ev.stop, 0, one);
+      else if (L.cfg == TILE_W4A8_N128 && p.gated)
+        hipExtLaunchKernelGGL((k_grouped_gemm_w4a8<64, 128, 2, 2, true, 2>), g, dim3(256), 0, st,
+                              ev.start, ev.stop, 0, one);
+      else if (L.cfg == TILE_W4A8_N128)
+        hipExtLaunchKernelGGL((k_grouped_gemm_w4a8<64, 128, 2, 2, false, 2>), g, dim3(256), 0, st,
                               ev.start, ev.stop, 0, one);
       else if (p.gated)
         hipExtLaunchKernelGGL((k_grouped_gemm_w4a8<128, 128, 2, 4, true, 1>), g, dim3(512), 0, st,

@@ -109,7 +109,7 @@ hipError_t launch_tile_tables(const int32_t* offsets, int E, const TileJobs& job
 hipError_t launch_mx_e4m3_quantize(const void* x, const int32_t* row_index, int64_t R, int K,
                                    uint8_t* codes, uint8_t* scales, hipStream_t s);
 // Plan of an FP4 x FP8 grouped GEMM (one segment of MXFP4 weights, K % 128 == 0);
-// 128-row tiles above 96 rows per group, else 64-row tiles.
+// 128-row tiles above 96 rows per group, else 64-row tiles (128 or 64 features).
 GemmPlan plan_w4a8_gemm(const SegShape& seg, bool gated, int64_t rows_per_group_hint);
 
 // Host planning of a grouped GEMM (tile shape, launches, table sizes).

@@ -98,7 +98,8 @@ def test_grouped_ffn_w4a8_vs_oracle(glu):
 
 
 def test_grouped_ffn_w4a8_rows_equal_in_any_batch():
-    """100 rows per expert take 128-row tiles, the smaller batches 64-row tiles."""
+    """100 rows per expert take 128 x 128 tiles, 20 rows 64 x 128, 0 rows 64 x 64:
+    the same bits in each."""
     banner("w4a8 batch invariance")
     E, D, I = 4, 256, 128
     m = _experts(95, E, D, I)
@@ -119,7 +120,8 @@ def test_layer_w4a8_vs_composed_oracle_and_invariance():
     """moe_layer_forward with MOE_FLAG_W4A8: routing, the FP4 x FP8 routed
     experts, the bf16 shared expert and the combine, against the oracle's
     stages composed; a token's row is the same bits at every T, across the
-    128-row and 64-row tiles (routed FP4 x FP8 and shared bf16 alike)."""
+    three FP4 x FP8 tile shapes and the shared expert's 128- and 64-row
+    bf16 tiles."""
     banner("w4a8 layer")
     E, k, D, I, Is, T = 8, 2, 256, 128, 128, 400  # 100 rows per expert: 128-row tiles
     m = _experts(97, E, D, I)
