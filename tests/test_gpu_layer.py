@@ -312,6 +312,37 @@ def test_tile_brackets_and_weight_formats_bitwise():
             assert np.array_equal(ys["bf16"], y_all[:T]), T
 
 
+def test_layer_w4a8_full_size_sampled():
+    """Recipe 5 at full size with MOE_FLAG_W4A8 (the launch configuration of
+    bench.py --config 5 --w4a8); the oracle recomputes a sample of tokens
+    stage by stage: hash routing, the FP4 x FP8 routed experts, the bf16 shared
+    expert, the combine."""
+    cfg = synth.CONFIGS[5]
+    banner(f"layer cfg5 W4A8 full T={cfg.T} (sampled oracle)")
+    dl, _ = _device_layer(5)
+    layer = sdev.layer_object(dl, w4a8=True)
+    x = synth.x_tokens(cfg)
+    ids = synth.token_ids(cfg)
+    y = to_np(layer.forward(dev(x), dev(ids)))
+    rng = np.random.default_rng(55)
+    sample = np.sort(rng.choice(cfg.T, size=3, replace=False))  # ~24 experts, ~2 s each
+    sample[-1] = cfg.T - 1  # the ragged end
+    n = len(sample)
+    xs, ids_s = np.ascontiguousarray(x[sample]), np.ascontiguousarray(ids[sample])
+    idx_s, w_s = oracle.route(None, None, ids_s, n, cfg.E, cfg.k, "hash")
+    _, offs, row_tok, pair_row = oracle.permute(idx_s, cfg.E)
+    o = np.empty((n * cfg.k, cfg.D), np.uint16)
+    for e in np.unique(idx_s):
+        a, b = offs[e], offs[e + 1]
+        o[a:b] = oracle.expert_ffn_w4a8(np.ascontiguousarray(xs[row_tok[a:b]]),
+                                        *synth.expert_matrices(cfg, int(e)))
+    s = oracle.expert_ffn(xs, *synth.shared_matrices(cfg), "bf16")
+    y_ref = oracle.combine(o, idx_s, w_s, pair_row, s, n, cfg.k, cfg.D)
+    r = rel_l2(y[sample], y_ref)
+    banner(f"cfg5 W4A8 sampled rel_l2={r:.3e}")
+    assert r <= 2e-3
+
+
 @pytest.mark.parametrize("cid,ntok", [(5, 12), (3, 12)])
 def test_layer_full_size_sampled(cid, ntok):
     """Full-size batch on the GPU; the oracle recomputes a sample of tokens."""
