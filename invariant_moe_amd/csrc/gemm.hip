@@ -41,6 +41,18 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 constexpr int KT = 64;         // K per LDS stage (two MFMA k-steps)
 
+// 16-byte weight load marked non-temporal (streamed past the caches' normal
+// replacement).  Used by the small-row tiles, where one m-tile covers all of
+// an expert's rows and so reads its weight panel exactly once: measured on
+// MI355X, decode steps 9-10 % faster (gate/up weights at 6.0 instead of
+// 5.4 TB/s); in 128-row prefill tiles, where several m-tiles of an expert
+// re-read the panel from L2, it is 6 % slower, so those keep plain loads.
+__device__ __forceinline__ uint4 nt_load16(const uint8_t* p) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // An LDS row holds one stage of one token or weight row: 64 bf16 = 128 B, no
 // padding.  Its eight 16-byte chunks are stored XOR-swizzled (chunk j of row r
 // at position j ^ (r & 7)), so that both the row-major staging writes and the
@@ -165,6 +177,7 @@ __global__ __launch_bounds__(64 * WM * WN, 2) void k_grouped_gemm_bf16(GemmArgs 
   constexpr int QPT = (QCH + NT - 1) / NT;
   constexpr int WQ = FP4 ? QPT : WPT;
   constexpr int BUF = (BM + NMAT * BN) * KT;  // bf16 elements of one LDS stage
+  constexpr bool kStreamW = BM <= 32;          // weights read once per launch: nt_load16
   __shared__ __align__(16) unsigned char smem[2 * BUF * 2];
 
   TileInfo ti;
@@ -273,7 +286,8 @@ __global__ __launch_bounds__(64 * WM * WN, 2) void k_grouped_gemm_bf16(GemmArgs 
         if (half && (none || (c % (KT / 8)) >= 4))
           wq[i] = make_uint4(0, 0, 0, 0);
         else
-          wq[i] = *reinterpret_cast<const uint4*>(wsrc[i] + (int64_t)k0 * 2);
+          wq[i] = kStreamW ? nt_load16(wsrc[i] + (int64_t)k0 * 2)
+                           : *reinterpret_cast<const uint4*>(wsrc[i] + (int64_t)k0 * 2);
       }
     } else {
 #pragma unroll
@@ -283,7 +297,8 @@ __global__ __launch_bounds__(64 * WM * WN, 2) void k_grouped_gemm_bf16(GemmArgs 
           wq[i] = make_uint4(0, 0, 0, 0);
           sq[i] = 127u;
         } else {
-          wq[i] = *reinterpret_cast<const uint4*>(wsrc[i] + k0 / 2);
+          wq[i] = kStreamW ? nt_load16(wsrc[i] + k0 / 2)
+                           : *reinterpret_cast<const uint4*>(wsrc[i] + k0 / 2);
           sq[i] = ssrc[i][k0 / 32];
         }
       }
@@ -547,6 +562,8 @@ __global__ __launch_bounds__(256) void k_grouped_gemm_f32(GemmArgs args) {
 //       the bf16 MFMA above.
 // LDS: token rows of a stage are 128 bytes, weight rows 64 bytes paired into
 // 128-byte lines; 16-byte chunks XOR-swizzled by line as in lds_off.
+// Weight loads are plain: non-temporal ones (nt_load16) measured 23 % slower
+// here with 8 rows per expert.
 // ---------------------------------------------------------------------------
 constexpr int KQ = 128;  // K per stage
 
