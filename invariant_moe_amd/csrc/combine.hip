@@ -228,7 +228,7 @@ __global__ __launch_bounds__(TPT > 256 ? TPT : 256) void k_residual_rmsnorm(Tail
   float part[Q];
 #pragma unroll
   for (int q = 0; q < Q; ++q) part[q] = 0.f;
-  float hreg[Q][8];  // round 0 (D <= 8 * kNormPartials) stays in registers
+  float hreg[Q][8];  // the first Q passes (D <= 8 * kNormPartials) stay in registers
   // h for the chunk at feature d (pass j): the row value (combine or x) plus
   // the residual, rounded; stored as the new residual and summed into its
   // partial.
