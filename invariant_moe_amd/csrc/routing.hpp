@@ -148,7 +148,11 @@ __device__ __forceinline__ bool topk_select(const float (&raw)[C], const float (
       my_val = ov;
     }
   }
-  const float top = readlane_f32(my_val, 0);
+  // Softmax shift: the largest selected logit (an exact maximum, so the same
+  // bits whatever the order).  With a bias the rank-0 expert need not hold it,
+  // and exp(l - l_rank0) could overflow.
+  float top = readlane_f32(my_val, 0);
+  for (int q = 1; q < k; ++q) top = fmaxf(top, readlane_f32(my_val, q));
   const bool act = lane < k;
   const float z = !act ? 0.0f
                        : (mode == MOE_ROUTE_SOFTMAX ? routing_exp(my_val - top) : my_val);

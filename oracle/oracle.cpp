@@ -222,7 +222,10 @@ void route_token(const float* logits, const float* bias, int32_t tid, int E, int
   }
   std::sort(asc.begin(), asc.end());
   if (mode == ROUTE_SOFTMAX) {
+    /* shift by the largest selected logit: softmax is shift-invariant, and
+     * with a bias the top-ranked expert need not hold the largest logit */
     float m = logits[idx[0]];
+    for (int j = 1; j < k; ++j) m = std::max(m, logits[idx[j]]);
     float Z = 0.0f;
     for (int j = 0; j < k; ++j) Z = Z + routing_exp(logits[asc[j]] - m);
     for (int j = 0; j < k; ++j) wout[j] = routing_exp(logits[idx[j]] - m) / Z;
@@ -627,6 +630,16 @@ int orc_num_threads(void) {
   return omp_get_max_threads();
 #else
   return 1;
+#endif
+}
+
+/* Threads of later parallel regions (n >= 1); the arithmetic of every output
+ * element is the same for any thread count. */
+void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
 #endif
 }
 

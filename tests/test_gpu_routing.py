@@ -166,3 +166,29 @@ def test_hash_routing_edges():
         ref_idx, ref_w = oracle.route(None, None, ids, len(ids), E, k, "hash")
         assert np.array_equal(to_np(idx), ref_idx)
         assert np.array_equal(to_np(w).view(np.uint32), ref_w.view(np.uint32))
+
+
+def test_softmax_bias_reorders_experts():
+    """Softmax routing where a bias ranks small logits first: the weights shift
+    by the largest selected logit (finite), bit-equal to the oracle.  Logits are
+    exact: x = e_0, W_r[e, 0] = the wanted logit (bf16-exact values)."""
+    banner("softmax with a reordering bias")
+    E, D, k, T = 64, 64, 4, 5
+    rng = np.random.default_rng(11)
+    lv = np.round(rng.uniform(-120, 120, size=(T, E))).astype(np.float32)
+    # token t: its own router row block -> use one W_r and per-token x = e_t
+    wr = np.zeros((E, D), np.float32)
+    x = np.zeros((T, D), np.float32)
+    for t in range(T):
+        x[t, t] = 1.0
+        wr[:, t] = lv[t]
+    bias = np.zeros(E, np.float32)
+    bias[:8] = 1000.0  # experts 0..7 always selected, whatever their logits
+    xb, wb = synth.f32_to_bf16(x), synth.f32_to_bf16(wr)
+    logits = oracle.router_logits(xb, wb)
+    assert np.array_equal(logits, lv)
+    ref_idx, ref_w = oracle.route(logits, bias, None, T, E, k, "softmax")
+    assert np.all(np.isfinite(ref_w))
+    idx, w = moe.router_topk(dev(xb), dev(wb), dev(bias), None, E, k, "softmax")
+    assert np.array_equal(to_np(idx), ref_idx)
+    assert np.array_equal(to_np(w).view(np.uint32), ref_w.view(np.uint32))
