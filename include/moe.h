@@ -139,7 +139,8 @@ typedef struct {
  *  p = degree-7 Taylor polynomial with fp32(1/j!) coefficients by Horner with
  *  fma, result p * 2^n (two exact scalings outside the normal range);
  *  x > 89 -> +inf, x < -104 -> +0.
- *   MOE_ROUTE_SOFTMAX: key = L (+ bias); w_j = exp(L_j - L_top) / Z.
+ *   MOE_ROUTE_SOFTMAX: key = L (+ bias); w_j = exp(L_j - L_max) / Z, L_max the
+ *                      largest logit among the k selected experts.
  *   MOE_ROUTE_SIGMOID: s = 1/(1 + exp(-L)) (IEEE division), key = s (+ bias);
  *                      w_j = s_j / Z.  The bias only decides selection.
  *   Z sums the selected terms in ascending expert id, in fp32, from +0.
@@ -324,6 +325,10 @@ int moe_set_stage_events(void* const* events, int n_events);
 const char* moe_status_string(int status);
 const char* moe_last_error(void); /* thread-local message of the last non-OK return */
 int moe_abi_version(void);
+/* Identifier of the sources this binary was built from (16 hex digits of a
+ * hash over the kernel and host sources, this header and the build flags),
+ * so that a caller can refuse a binary built from other sources. */
+const char* moe_build_id(void);
 
 #ifdef __cplusplus
 }

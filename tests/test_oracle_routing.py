@@ -186,3 +186,43 @@ def test_permute_is_stable_counting_sort():
         assert np.array_equal(counts, np.bincount(idx.ravel(), minlength=E))
         assert offsets[0] == 0 and offsets[E] == T * k
         assert np.array_equal(np.diff(offsets), counts)
+
+
+def test_hash_slots_from_published_fmix32_values():
+    """Slot j of token tid hashes tid + j * 0x9E3779B9; for the token ids of
+    tests/golden/hash_slots.txt that argument is an input whose fmix32 value is
+    published, so the slot's expert is known without the oracle's hash."""
+    cases = read_golden("hash_slots.txt")
+    assert len(cases) >= 6
+    for ln in cases:
+        tid, E, k, j, inp, want = ln.split()
+        tid_u, E, k, j, want = int(tid, 16), int(E), int(k), int(j), int(want)
+        assert (tid_u + j * 0x9E3779B9) % (1 << 32) == int(inp, 16)
+        ids = np.array([tid_u], dtype=np.uint32).view(np.int32)
+        idx, w = oracle.route(None, None, ids, 1, E, k, "hash")
+        assert want not in list(idx[0, :j]), ln  # no earlier slot took it: no probing
+        assert idx[0, j] == want, (ln, idx[0])
+        assert np.all(w == np.float32(1.0 / k))
+
+
+def test_softmax_shift_is_the_largest_selected_logit():
+    """A bias can rank an expert with a small logit first; the weights must
+    still be the renormalised softmax over the selected logits (finite, summing
+    to 1).  Shifting by the rank-0 logit would give exp(100) = inf here."""
+    E, k = 6, 3
+    logits = np.array([[0.0, 100.0, 99.0, -5.0, 3.0, 1.0]], dtype=np.float32)
+    bias = np.zeros(E, dtype=np.float32)
+    bias[0] = 1000.0  # expert 0 (logit 0) ranks first
+    idx, w = oracle.route(logits, bias, None, 1, E, k, "softmax")
+    assert list(idx[0]) == [0, 1, 2]
+    assert np.all(np.isfinite(w))
+    sel = logits[0, idx[0]].astype(np.float64)
+    ref = np.exp(sel - sel.max())
+    ref /= ref.sum()
+    assert np.allclose(w[0], ref, rtol=2e-6, atol=1e-30)
+    assert abs(float(w[0].astype(np.float64).sum()) - 1.0) <= k * 2.0**-23
+    # without a bias the shift is the rank-0 logit, as before
+    idx2, w2 = oracle.route(logits, None, None, 1, E, k, "softmax")
+    assert list(idx2[0]) == [1, 2, 4]
+    ref2 = np.exp(logits[0, [1, 2, 4]].astype(np.float64) - 100.0)
+    assert np.allclose(w2[0], ref2 / ref2.sum(), rtol=2e-6)
