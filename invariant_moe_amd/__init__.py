@@ -8,6 +8,8 @@ fallback — if the library is missing, loading it raises.
 from __future__ import annotations
 
 import ctypes
+import functools
+import inspect
 import os
 from dataclasses import dataclass
 from typing import Optional
@@ -29,7 +31,8 @@ EXPORTS = ("moe_router_workspace_bytes", "moe_router_topk", "moe_routing_scores"
            "moe_grouped_swiglu_w4a8",
            "moe_combine", "moe_residual_rmsnorm", "moe_combine_rmsnorm",
            "moe_layer_workspace_bytes", "moe_layer_forward",
-           "moe_set_stage_events", "moe_status_string", "moe_last_error", "moe_abi_version")
+           "moe_set_stage_events", "moe_status_string", "moe_last_error", "moe_abi_version",
+           "moe_build_id")
 
 
 class MoEError(RuntimeError):
@@ -83,6 +86,7 @@ def lib() -> ctypes.CDLL:
         L.moe_status_string.argtypes = [i32]
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_last_error.restype = ctypes.c_char_p
+        L.moe_build_id.restype = ctypes.c_char_p
         for name in ("moe_router_topk", "moe_routing_scores", "moe_permute", "moe_grouped_swiglu", "moe_combine",
                      "moe_residual_rmsnorm", "moe_combine_rmsnorm", "moe_layer_forward",
                      "moe_mx_e4m3_quantize", "moe_grouped_swiglu_w4a8",
@@ -90,6 +94,21 @@ def lib() -> ctypes.CDLL:
             getattr(L, name).restype = i32
         _lib = L
     return _lib
+
+
+def build_id() -> str:
+    """Source hash compiled into the loaded library (moe_build_id)."""
+    return lib().moe_build_id().decode()
+
+
+def check_build() -> None:
+    """Raise if the loaded library was built from other sources than the ones
+    next to it (a stale binary)."""
+    from . import _build
+    want, got = _build.source_hash(), build_id()
+    if want != got:
+        raise MoEError(f"{LIB_PATH} was built from other sources (build id {got}, sources "
+                       f"{want}): rebuild it with __graft_entry__.build()")
 
 
 def _check(rc: int) -> None:
@@ -122,6 +141,35 @@ def _stream(stream) -> int:
     return stream.cuda_stream
 
 
+def _on(stream):
+    """Allocation context of a call: buffers (workspaces, outputs) are taken
+    from the caching allocator on the stream the kernels run on, so a buffer
+    released when the call returns is reused only after that stream's work."""
+    return torch.cuda.stream(stream) if stream is not None else _nullctx()
+
+
+class _nullctx:
+    def __enter__(self):
+        return None
+
+    def __exit__(self, *exc):
+        return False
+
+
+def _allocating(fn):
+    """Runs an entry point with the caching allocator on its `stream` argument
+    (see _on): the workspace it drops and the outputs it returns belong to the
+    stream its kernels were enqueued on."""
+    sig = inspect.signature(fn)
+
+    @functools.wraps(fn)
+    def wrapper(*args, **kw):
+        b = sig.bind(*args, **kw)
+        with _on(b.arguments.get("stream")):
+            return fn(*args, **kw)
+    return wrapper
+
+
 @dataclass
 class ExpertWeights:
     """Weights of G experts: gate/up [G, I, D], down [G, D, I] (bf16 or fp32 tensors),
@@ -149,6 +197,7 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
+@_allocating
 def router_topk(x, w_router, bias, token_ids, E: int, k: int, mode: str, stream=None):
     """Routing: returns (topk_idx [T,k] int32, topk_w [T,k] fp32)."""
     if mode == "hash":
@@ -168,6 +217,7 @@ def router_topk(x, w_router, bias, token_ids, E: int, k: int, mode: str, stream=
     return idx, w
 
 
+@_allocating
 def routing_scores(logits, mode: str, out=None, stream=None):
     """Elementwise routing sigmoid (mode "sigmoid") or routing exp ("softmax")."""
     if out is None:
@@ -177,6 +227,7 @@ def routing_scores(logits, mode: str, out=None, stream=None):
     return out
 
 
+@_allocating
 def permute(topk_idx, E: int, x=None, stream=None):
     """Dispatch: returns (counts [E], offsets [E+1], row_token [T*k], pair_row [T*k],
     x_perm [T*k, D] or None)."""
@@ -200,6 +251,7 @@ def permute(topk_idx, E: int, x=None, stream=None):
     return counts, offsets, row_token, pair_row, x_perm
 
 
+@_allocating
 def grouped_swiglu(x_rows, row_index, expert_offsets, R: int, E: int, weights: ExpertWeights,
                    out=None, stream=None, glu: str = "swiglu"):
     """Expert FFN over grouped rows: out [R, D].  glu: "swiglu", "clamp" or "situ"."""
@@ -218,6 +270,7 @@ def grouped_swiglu(x_rows, row_index, expert_offsets, R: int, E: int, weights: E
     return out
 
 
+@_allocating
 def mx_e4m3_quantize(x, row_index=None, R=None, stream=None):
     """MXFP8 (E4M3 + E8M0 per 32) codes [R, K] and scales [R, K/32] of bf16 rows
     x[row_index[r]] (or x[r])."""
@@ -231,6 +284,7 @@ def mx_e4m3_quantize(x, row_index=None, R=None, stream=None):
     return codes, scales
 
 
+@_allocating
 def grouped_swiglu_w4a8(x_rows, row_index, expert_offsets, R: int, E: int,
                         weights: ExpertWeights, out=None, stream=None, glu: str = "swiglu"):
     """Expert FFN over grouped rows with MXFP4 weights and MXFP8 activations:
@@ -250,6 +304,7 @@ def grouped_swiglu_w4a8(x_rows, row_index, expert_offsets, R: int, E: int,
     return out
 
 
+@_allocating
 def combine(expert_out, topk_idx, topk_w, pair_row, shared_out, out=None, stream=None):
     """Weighted combine: y [T, D]."""
     T, k = topk_idx.shape
@@ -262,6 +317,7 @@ def combine(expert_out, topk_idx, topk_w, pair_row, shared_out, out=None, stream
     return out
 
 
+@_allocating
 def residual_rmsnorm(x, residual, gamma, eps: float, residual_out=None, normed=None,
                      stream=None):
     """h = round(x + residual) -> residual_out, RMSNorm(h) * gamma -> normed.
@@ -276,6 +332,7 @@ def residual_rmsnorm(x, residual, gamma, eps: float, residual_out=None, normed=N
     return residual_out, normed
 
 
+@_allocating
 def combine_rmsnorm(expert_out, topk_idx, topk_w, pair_row, shared_out, residual, gamma,
                     eps: float, residual_out=None, normed=None, stream=None):
     """The combine fused with residual_rmsnorm of its output (same bits as the two
@@ -297,6 +354,7 @@ def layer_workspace_bytes(T, D, E, k, I, I_shared, act, wdtype) -> int:
     return lib().moe_layer_workspace_bytes(T, D, E, k, I, I_shared, act, wdtype)
 
 
+@_allocating
 def layer_forward(x, token_ids, w_router, bias, routed: ExpertWeights,
                   shared: Optional[ExpertWeights], E: int, k: int, mode: str, out=None,
                   workspace=None, stream=None, glu: str = "swiglu", w4a8: bool = False):
@@ -337,21 +395,30 @@ def set_stage_events(events) -> None:
 
 
 class MoELayer:
-    """Device-resident layer weights plus a reusable workspace."""
+    """Device-resident layer weights plus one reusable workspace per stream.
+
+    Calls on one stream run in order and share that stream's workspace; calls
+    on different streams use different workspaces, so they may overlap.  A
+    workspace that grows is replaced after the old one's stream has finished
+    with it (the allocator reuses a block only after its stream's work)."""
 
     def __init__(self, w_router, bias, routed: ExpertWeights, shared: Optional[ExpertWeights],
                  E: int, k: int, mode: str, glu: str = "swiglu", w4a8: bool = False):
         self.w_router, self.bias, self.routed, self.shared = w_router, bias, routed, shared
         self.E, self.k, self.mode, self.glu, self.w4a8 = E, k, mode, glu, w4a8
-        self._ws = None
+        self._ws = {}  # stream handle -> workspace allocated on that stream
 
     def forward(self, x, token_ids=None, out=None, stream=None):
         T, D = x.shape
         I = self.routed.gate.shape[1]
         Is = self.shared.gate.shape[1] if self.shared is not None else 0
         nb = layer_workspace_bytes(T, D, self.E, self.k, I, Is, _act(x), self.routed.dtype) + 256
-        if self._ws is None or self._ws.numel() < nb:
-            self._ws = _workspace(nb, x.device)
+        st = stream if stream is not None else torch.cuda.current_stream()
+        ws = self._ws.get(st.cuda_stream)
+        if ws is None or ws.numel() < nb:
+            with _on(st):
+                ws = _workspace(nb, x.device)
+            self._ws[st.cuda_stream] = ws
         return layer_forward(x, token_ids, self.w_router, self.bias, self.routed, self.shared,
-                             self.E, self.k, self.mode, out=out, workspace=self._ws,
-                             stream=stream, glu=self.glu, w4a8=self.w4a8)
+                             self.E, self.k, self.mode, out=out, workspace=ws,
+                             stream=st, glu=self.glu, w4a8=self.w4a8)

@@ -12,6 +12,10 @@
 #include "../../include/moe.h"
 #include "kernels.hpp"
 
+#ifndef MOE_BUILD_ID
+#define MOE_BUILD_ID "unversioned"
+#endif
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -273,6 +277,8 @@ moe::GemmSeg make_seg(const void* A, const int32_t* a_index, const int32_t* offs
 extern "C" {
 
 int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_build_id(void) { return MOE_BUILD_ID; }
 
 const char* moe_last_error(void) { return g_err; }
 

@@ -18,6 +18,16 @@ def pytest_configure(config):
         ge._build_synth()
     if not os.path.exists(os.path.join(ROOT, "oracle", "liboracle.so")):
         ge._build_oracle()
+    # The HIP library: built when missing; a binary built from other sources
+    # than the checked-out ones stops the run (no test may pass on it).
+    import invariant_moe_amd as moe
+    if not os.path.exists(moe.LIB_PATH):
+        from invariant_moe_amd import _build
+        _build.build_library()
+    try:
+        moe.check_build()
+    except moe.MoEError as e:
+        raise pytest.UsageError(str(e))
 
 
 def golden_path(name):

@@ -28,6 +28,16 @@ def test_library_exports_every_declared_symbol():
     assert L.moe_abi_version() == 3
 
 
+def test_build_id_matches_sources():
+    """The loaded binary carries the hash of the sources it was built from;
+    it equals the hash of the checked-out sources (no stale binary)."""
+    from invariant_moe_amd import _build
+    got = moe.build_id()
+    assert len(got) == 16 and int(got, 16) >= 0
+    assert got == _build.source_hash()
+    moe.check_build()
+
+
 def test_status_strings():
     L = moe.lib()
     assert L.moe_status_string(0) == b"MOE_OK"
