@@ -69,6 +69,8 @@ def lib():
                                         i64, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, i32]
         L.orc_layer_forward.restype = i32
         L.orc_num_threads.restype = i32
+        L.orc_set_num_threads.argtypes = [i32]
+        L.orc_set_num_threads.restype = None
         _lib = L
     return _lib
 
@@ -268,3 +270,8 @@ def layer_forward(x, token_ids, w_router, bias, experts: dict, shared, T, D, E, 
 
 def num_threads() -> int:
     return lib().orc_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's later calls (the results do not depend on it)."""
+    lib().orc_set_num_threads(int(n))

@@ -49,9 +49,15 @@ class DeviceLayer:
     sh_gate: Optional[torch.Tensor]
     sh_up: Optional[torch.Tensor]
     sh_down: Optional[torch.Tensor]
+    host_experts: Optional[dict] = None  # expert id -> host matrices kept by upload_layer
 
 
-def upload_layer(cfg: synth.LayerConfig, device="cuda") -> DeviceLayer:
+def upload_layer(cfg: synth.LayerConfig, device="cuda", keep_experts=(),
+                 progress=None) -> DeviceLayer:
+    """Generates the layer's weights expert by expert and copies them to the
+    device; the host matrices of the experts in keep_experts are kept (for a
+    CPU computation on the same bytes without generating them again).
+    progress(e, E), if given, is called every 64 experts."""
     E, I, D = cfg.E, cfg.I, cfg.D
     mx = cfg.wdtype == "mxfp4"
     if mx:
@@ -68,8 +74,13 @@ def upload_layer(cfg: synth.LayerConfig, device="cuda") -> DeviceLayer:
         up = torch.empty_like(gate)
         down = torch.empty((E, D, I), dtype=tdt, device=device)
         gs = us = ds = None
+    kept = {}
     for e in range(E):
+        if progress is not None and e % 64 == 0 and e:
+            progress(e, E)
         g, u, d = synth.expert_matrices(cfg, e)
+        if e in keep_experts:
+            kept[e] = (g, u, d)
         if mx:
             gate[e].copy_(torch.from_numpy(g[0]))
             gs[e].copy_(torch.from_numpy(g[1]))
@@ -90,7 +101,7 @@ def upload_layer(cfg: synth.LayerConfig, device="cuda") -> DeviceLayer:
         wr = _to_dev(synth.router_weight(cfg), device)
         b = synth.router_bias(cfg)
         bias = None if b is None else torch.from_numpy(b).to(device)
-    return DeviceLayer(cfg, wr, bias, gate, up, down, gs, us, ds, shg, shu, shd)
+    return DeviceLayer(cfg, wr, bias, gate, up, down, gs, us, ds, shg, shu, shd, kept)
 
 
 def layer_object(dl: DeviceLayer, glu: str = "swiglu", w4a8: bool = False):

@@ -35,8 +35,9 @@ _layers = {}
 def _device_layer(cid):
     if cid not in _layers:
         cfg = synth.CONFIGS[cid]
-        dl = sdev.upload_layer(cfg, "cuda")
         _layers.clear()  # keep one large layer resident at a time
+        dl = sdev.upload_layer(cfg, "cuda",
+                               progress=lambda e, n: banner(f"recipe {cid}: {e}/{n} experts"))
         _layers[cid] = (dl, sdev.layer_object(dl))
     return _layers[cid]
 
@@ -201,6 +202,34 @@ def test_determinism_repeat_and_streams():
         c = layer.forward(x, stream=s)
     s.synchronize()
     assert np.array_equal(a, b) and np.array_equal(a, to_np(c))
+
+
+def test_side_streams_not_current():
+    """forward on streams that are not the current one: each stream gets its
+    own workspace and its outputs are allocated on it, so two calls in flight
+    on two streams do not share memory; results equal the current stream's."""
+    cfg = synth.CONFIGS[2]
+    banner("side streams")
+    dl, _ = _device_layer(2)
+    layer = sdev.layer_object(dl)
+    xa = dev(synth.x_tokens(cfg, T=300))
+    xb = dev(synth.x_tokens(cfg, T=200, offset_tokens=300))
+    ya, yb = to_np(layer.forward(xa)), to_np(layer.forward(xb))
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    outs = []
+    for _ in range(3):  # interleaved, no synchronisation between the streams
+        outs.append((layer.forward(xa, stream=s1), layer.forward(xb, stream=s2)))
+    s1.synchronize()
+    s2.synchronize()
+    assert len(layer._ws) >= 3  # current stream, s1, s2
+    for a, b in outs:
+        assert np.array_equal(to_np(a), ya) and np.array_equal(to_np(b), yb)
+    # the plain entry points on a side stream
+    idx, w = moe.router_topk(xa, dl.w_router, dl.bias, None, cfg.E, cfg.k, "sigmoid", stream=s1)
+    s1.synchronize()
+    ridx, rw = moe.router_topk(xa, dl.w_router, dl.bias, None, cfg.E, cfg.k, "sigmoid")
+    assert torch.equal(idx, ridx) and torch.equal(w, rw)
 
 
 def test_mxfp4_equals_bf16_on_decoded_weights():
