@@ -4,15 +4,16 @@
 
 A step is one moe_layer_forward (routing, permutation, gate/up SwiGLU GEMM,
 down GEMM, combine) over one batch of seeded synthetic tokens whose inputs are
-already resident in HBM.  The default workload is the small bf16 layer
-(T=512, D=1024, E=64 routed + 1 shared expert, top-6 sigmoid routing, expert
-inter dim 512).  Several replicas of the expert weights are rotated across
-steps so that the 256 MB last-level cache cannot hold the weights between
-steps.
+already resident in HBM.  The default workload is the DeepSeek-V3-shaped
+prefill layer: T=4096 tokens, D=7168, E=256 routed + 1 shared expert, top-8
+sigmoid routing with a Zipf(1.1) bias, expert inter dim 2048, bf16 (22.5 GB of
+expert weights, far past the 256 MB last-level cache).  Smaller layers rotate
+several weight replicas across steps so that the cache cannot hold them.
 
-Prints ONE JSON line with throughput (tokens/s), the roofline of the dominant
-kernel (the gate/up SwiGLU GEMM) measured with HIP events recorded between the
-stages of every timed step, and the CPU oracle timed on the host.
+Prints ONE JSON line: throughput (tokens/s), the roofline of the dominant
+kernel (the gate/up SwiGLU GEMM, timed with HIP events at the kernel's own
+start and end), the step-time spread, the clocks during the timed steps, the
+decode sweep on the same weights, and the CPU oracle timed on the host.
 """
 from __future__ import annotations
 
@@ -31,7 +32,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA (FP4 x FP8 runs at the FP8 rate)
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "gate_up_gemm_traffic.json")
+PROFILES = os.path.join(ROOT, "profiles")
 
 
 def parse():
@@ -39,7 +40,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--config", type=int, default=2, help="layer recipe (1..5), default 2")
+    p.add_argument("--config", type=int, default=3,
+                   help="layer recipe (1..5), default 3 (DeepSeek-V3-shaped prefill)")
     p.add_argument("--T", type=int, default=None, help="override the batch size")
     p.add_argument("--replicas", type=int, default=0, help="weight replicas (0 = auto)")
     p.add_argument("--w4a8", action="store_true",
@@ -50,11 +52,18 @@ def parse():
                                                           "CAL_FETCH_CSV", "CAL_WRITE_CSV"),
                    help="turn rocprofv3 --pmc counter CSVs (FETCH_SIZE run, WRITE_SIZE run, and "
                         "the same two counters over --copy-calibration) into the gate/up GEMM "
-                        "HBM bytes per launch; writes profiles/gate_up_gemm_traffic.json")
+                        "HBM bytes per launch of the --config/--T workload; writes "
+                        "profiles/gate_up_gemm_traffic_recipe<N>_T<T>.json")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="approximate CPU time budget of the oracle baseline (0 = skip)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (counter calibration)")
+    p.add_argument("--gemm-only", action="store_true",
+                   help="time the layer only (no tail, W4A8, decode sweep or CPU baseline); "
+                        "for counter passes")
+    p.add_argument("--decode-T", default="1,2,4,8,16,32,64",
+                   help="decode batch sizes timed on the same weights (layers of the "
+                        "DeepSeek-V3 shape only; empty = none)")
     return p.parse_args()
 
 
@@ -91,11 +100,16 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(per_launch_bytes_alg: float):
+def traffic_path(cfg) -> str:
+    return os.path.join(PROFILES, f"gate_up_gemm_traffic_recipe{cfg.cid}_T{cfg.T}.json")
+
+
+def measured_traffic(cfg):
     """HBM bytes per launch of the gate/up GEMM from the committed rocprofv3
-    counter summary, if it was taken on the current kernel source."""
+    counter summary of this workload, if it was taken on the current kernel
+    source (else None)."""
     try:
-        with open(PROFILE_TRAFFIC) as f:
+        with open(traffic_path(cfg)) as f:
             d = json.load(f)
     except (OSError, ValueError):
         return None
@@ -114,7 +128,7 @@ def _counter_means(path, counter, name_pred):
     return vals
 
 
-def traffic_summary(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv):
+def traffic_summary(cfg, fetch_csv, write_csv, cal_fetch_csv, cal_write_csv):
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the gate/up GEMM, each
     scaled by the bytes a 1 GiB device copy really moves over what the same
     counter reports for it."""
@@ -132,6 +146,7 @@ def traffic_summary(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv):
     fetch = sum(f) / len(f) * 1024.0 * kf
     write = sum(w) / len(w) * 1024.0 * kw
     d = {"kernel": "k_grouped_gemm_bf16 gate/up (gated) launch",
+         "workload": f"recipe {cfg.cid} ({cfg.name}) T={cfg.T}",
          "kernel_source_hash": kernel_source_hash(),
          "dispatches": [len(f), len(w)],
          "fetch_size_kib_avg": round(sum(f) / len(f), 1),
@@ -139,7 +154,7 @@ def traffic_summary(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv):
          "copy_factor_fetch": round(kf, 4), "copy_factor_write": round(kw, 4),
          "fetch_bytes_per_launch": int(fetch), "write_bytes_per_launch": int(write),
          "bytes_per_launch": int(fetch + write)}
-    with open(PROFILE_TRAFFIC, "w") as fh:
+    with open(traffic_path(cfg), "w") as fh:
         json.dump(d, fh, indent=1)
         fh.write("\n")
     print(json.dumps(d))
@@ -261,6 +276,165 @@ def w4a8_measurement(dl, x, ids, hip, sptr, steps: int):
                       "k_grouped_gemm_bf16 on decoded MXFP4"}
 
 
+class ClockSampler:
+    """Samples the GPU's current shader and memory clock levels (sysfs
+    pp_dpm_sclk / pp_dpm_mclk, the entry marked '*') on a host thread while
+    the timed steps run.  Gives None where sysfs does not expose them."""
+
+    def __init__(self, period_s=0.02):
+        import glob
+        import threading
+        self.period = period_s
+        self.paths = None
+        cands = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        dev = self._pci_dir()
+        if dev and os.path.exists(os.path.join(dev, "pp_dpm_sclk")):
+            self.paths = (os.path.join(dev, "pp_dpm_sclk"), os.path.join(dev, "pp_dpm_mclk"))
+        elif len(cands) == 1:
+            d = os.path.dirname(cands[0])
+            self.paths = (cands[0], os.path.join(d, "pp_dpm_mclk"))
+        self.samples = {"sclk": [], "mclk": []}
+        self._stop = threading.Event()
+        self._thr = threading.Thread(target=self._run, daemon=True)
+
+    @staticmethod
+    def _pci_dir():
+        try:
+            import torch
+            p = torch.cuda.get_device_properties(0)
+            dom, bus, dev = p.pci_domain_id, p.pci_bus_id, p.pci_device_id
+            return f"/sys/bus/pci/devices/{dom:04x}:{bus:02x}:{dev:02x}.0"
+        except Exception:
+            return None
+
+    @staticmethod
+    def _current_mhz(path):
+        with open(path) as f:
+            for ln in f:
+                if ln.rstrip().endswith("*"):
+                    v = ln.split(":", 1)[1].strip().rstrip("*").strip().lower()
+                    return float(v.replace("mhz", ""))
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            for key, path in zip(("sclk", "mclk"), self.paths):
+                try:
+                    v = self._current_mhz(path)
+                    if v is not None:
+                        self.samples[key].append(v)
+                except (OSError, ValueError):
+                    pass
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.paths:
+            self._thr.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self.paths:
+            self._stop.set()
+            self._thr.join()
+        return False
+
+    def summary(self):
+        import numpy as np
+        out = {"source": "sysfs pp_dpm_sclk / pp_dpm_mclk (current level)" if self.paths
+               else None}
+        for key, v in self.samples.items():
+            out[key + "_mhz"] = ({"median": float(np.median(v)), "min": float(min(v)),
+                                  "max": float(max(v)), "samples": len(v)} if v else None)
+        return out
+
+
+def stream_copy_gbs(hip, sptr, nbytes=4 << 30, reps=10):
+    """Achievable HBM bandwidth of a plain device copy (bytes read + written
+    over time), measured beside the layer with the same events."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(2):
+        b.copy_(a)
+    e0, e1 = hip.event(), hip.event()
+    torch.cuda.synchronize()
+    hip.record(e0, sptr)
+    for _ in range(reps):
+        b.copy_(a)
+    hip.record(e1, sptr)
+    torch.cuda.synchronize()
+    ms = hip.elapsed_ms(e0, e1) / reps
+    del a, b
+    return round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
+
+
+def decode_sweep(cfg3, layer, hip, sptr, Ts, steps: int):
+    """The DeepSeek-V3-shaped layer at decode batch sizes on the resident
+    weights: the 64-token decode pool (seeded), one window of T tokens per step,
+    windows rotating over the pool so consecutive steps touch different experts.
+    Algorithmic bytes per step: the experts the window touches, read once
+    (3*I*D*2 each), the shared expert, the router, x and y."""
+    import numpy as np
+    import torch
+
+    import invariant_moe_amd as moe
+    import synth
+    from synth import device as sdev
+
+    cfg4 = synth.CONFIGS[4]
+    pool = synth.x_tokens(cfg4)  # 64 tokens
+    D, E, k, I, Is = cfg3.D, cfg3.E, cfg3.k, cfg3.I, cfg3.I_shared
+    res = []
+    for T in Ts:
+        nwin = 16
+        xs, U = [], []
+        for w in range(nwin):
+            rows = (np.arange(T) + w * max(T, 4)) % pool.shape[0]
+            x = sdev.bf16_tensor(np.ascontiguousarray(pool[rows]), "cuda")
+            idx, _ = moe.router_topk(x, layer.w_router, layer.bias, None, E, k, "sigmoid")
+            U.append(int(torch.unique(idx).numel()))
+            xs.append(x)
+        y = torch.empty((T, D), dtype=torch.bfloat16, device="cuda")
+        for i in range(5):
+            layer.forward(xs[i % nwin], out=y)
+        e0, e1 = hip.event(), hip.event()
+        torch.cuda.synchronize()
+        hip.record(e0, sptr)
+        for i in range(steps):
+            layer.forward(xs[i % nwin], out=y)
+        hip.record(e1, sptr)
+        torch.cuda.synchronize()
+        ms = hip.elapsed_ms(e0, e1) / steps
+        u = float(np.mean([U[i % nwin] for i in range(steps)]))
+        nbytes = u * 3 * I * D * 2 + 3 * Is * D * 2 + E * D * 2 + E * 4 + 2 * T * D * 2
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res.append({"T": T, "ms": round(ms, 5), "experts_touched": round(u, 2),
+                    "alg_bytes": int(nbytes), "gbs": round(gbs, 1),
+                    "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                    "tokens_per_s": round(T / (ms * 1e-3), 1)})
+    return res
+
+
+def cpu_info():
+    model, smt = None, None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        with open("/sys/devices/system/cpu/smt/active") as f:
+            smt = f.read().strip() == "1"
+    except OSError:
+        pass
+    return {"cpu_model": model, "smt_active": smt, "online_cpus": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -270,32 +444,63 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
-    if args.traffic_summary:
-        traffic_summary(*args.traffic_summary)
-        return
 
     import numpy as np
-    import torch
 
-    import invariant_moe_amd as moe
     import synth
-    from synth import device as sdev
 
     cfg = synth.CONFIGS[args.config]
     if args.T is not None:
         cfg = cfg.with_T(args.T)
+    if args.traffic_summary:
+        traffic_summary(cfg, *args.traffic_summary)
+        return
     if args.w4a8 and cfg.wdtype != "mxfp4":
         print("bench.py: --w4a8 needs a recipe with MXFP4 routed weights (recipe 5)",
               file=sys.stderr)
         sys.exit(2)
+
+    import torch
+
+    import invariant_moe_amd as moe
+    from synth import device as sdev
+
+    moe.check_build()
+    T, D, E, k, I, Is = cfg.T, cfg.D, cfg.E, cfg.k, cfg.I, cfg.I_shared
+    R = T * k
+    es = 4 if cfg.act == "f32" else 2
+    cpu_on = args.cpu_seconds > 0 and not args.gemm_only
+
+    # The oracle's sample (first T_s tokens of the batch): its experts are kept
+    # on the host while the weights are generated, so the CPU baseline runs on
+    # the same bytes without generating them twice.
+    sample = None
+    if cpu_on:
+        import oracle
+        T_s = T if D * I * k <= 1 << 26 else min(8, T)
+        xs = np.ascontiguousarray(synth.x_tokens(cfg, T=T_s))
+        idsn = synth.token_ids(cfg, T=T_s) if cfg.route == "hash" else None
+        wr_h = synth.router_weight(cfg) if cfg.route != "hash" else None
+        bias_h = synth.router_bias(cfg)
+        if cfg.route == "hash":
+            s_idx, _ = oracle.route(None, None, idsn, T_s, E, k, "hash")
+        else:
+            s_idx, _ = oracle.route(oracle.router_logits(xs, wr_h), bias_h, None, T_s, E, k,
+                                    cfg.route)
+        sample = (T_s, xs, idsn, wr_h, bias_h, sorted(int(e) for e in np.unique(s_idx)))
+
     dev = "cuda:0"
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
     hip = Hip()
 
-    print(f"[bench] uploading recipe {cfg.cid} ({cfg.name}) T={cfg.T}", file=sys.stderr, flush=True)
-    dl = sdev.upload_layer(cfg, dev)
+    print(f"[bench] uploading recipe {cfg.cid} ({cfg.name}) T={T}", file=sys.stderr, flush=True)
+    t_up = time.perf_counter()
+    dl = sdev.upload_layer(cfg, dev, keep_experts=set(sample[5]) if sample else (),
+                           progress=lambda e, n: print(f"[bench] {e}/{n} experts uploaded",
+                                                       file=sys.stderr, flush=True))
+    print(f"[bench] uploaded in {time.perf_counter() - t_up:.1f} s", file=sys.stderr, flush=True)
     wbytes_routed = dl.gate.numel() * dl.gate.element_size() * 3  # gate + up + down (+pack)
     if dl.gate_scale is not None:
         wbytes_routed += 3 * dl.gate_scale.numel()
@@ -314,31 +519,42 @@ def main():
         layers.append(sdev.layer_object(c, args.glu, args.w4a8))
     x = sdev.x_device(cfg, dev)
     ids = sdev.token_ids_device(cfg, dev)
-    y = torch.empty((cfg.T, cfg.D), dtype=x.dtype, device=dev)
+    y = torch.empty((T, D), dtype=x.dtype, device=dev)
 
     # routing statistics of this batch (for the algorithmic byte count)
-    idx, _ = moe.router_topk(x, dl.w_router, dl.bias, ids, cfg.E, cfg.k, cfg.route)
-    counts = torch.bincount(idx.flatten().long(), minlength=cfg.E).cpu().numpy()
+    idx, _ = moe.router_topk(x, dl.w_router, dl.bias, ids, E, k, cfg.route)
+    counts = torch.bincount(idx.flatten().long(), minlength=E).cpu().numpy()
     U = int((counts > 0).sum())
 
     for i in range(args.warmup):
         layers[i % nrep].forward(x, ids, out=y)
     torch.cuda.synchronize()
+    print("[bench] warm-up done", file=sys.stderr, flush=True)
 
     K = args.steps
     # Pass 1 (the measurement): K steps with no instrumentation inside; one
-    # event pair and the host clock bracket them.
+    # event pair and the host clock bracket them; clocks sampled meanwhile.
     ev0, ev1 = hip.event(), hip.event()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    hip.record(ev0, sptr)
-    for i in range(K):
-        layers[i % nrep].forward(x, ids, out=y)
-    hip.record(ev1, sptr)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with ClockSampler() as clocks:
+        t0 = time.perf_counter()
+        hip.record(ev0, sptr)
+        for i in range(K):
+            layers[i % nrep].forward(x, ids, out=y)
+        hip.record(ev1, sptr)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     gpu_ms = hip.elapsed_ms(ev0, ev1)
     ms_per_step = max(wall * 1e3, gpu_ms) / K
+
+    # Pass 1b: one event between consecutive steps -> the spread of step times.
+    sev = [hip.event() for _ in range(K + 1)]
+    hip.record(sev[0], sptr)
+    for i in range(K):
+        layers[i % nrep].forward(x, ids, out=y)
+        hip.record(sev[i + 1], sptr)
+    torch.cuda.synchronize()
+    step_ms = np.array([hip.elapsed_ms(sev[i], sev[i + 1]) for i in range(K)])
 
     # Pass 2: the same steps with events between the stages (each event
     # record costs GPU time, so these sum to more than a step of pass 1).
@@ -360,21 +576,25 @@ def main():
         layers[i % nrep].forward(x, ids, out=y)
     moe.set_stage_events(None)
     torch.cuda.synchronize()
-    try:
-        kern_ms = np.array([[hip.elapsed_ms(kev[i][6], kev[i][7]),
-                             hip.elapsed_ms(kev[i][8], kev[i][9])] for i in range(K2)]).mean(0)
-    except AssertionError:  # a library without kernel events: stage times instead
-        kern_ms = stage_avg[[2, 3]]
+    kern_ms = np.array([[hip.elapsed_ms(kev[i][6], kev[i][7]),
+                         hip.elapsed_ms(kev[i][8], kev[i][9])] for i in range(K2)]).mean(0)
     gu_ms = float(kern_ms[0])
+    print("[bench] layer timed", file=sys.stderr, flush=True)
 
-    tail = tail_measurement(cfg, hip, sptr, min(K, 50))
-    w4a8 = (w4a8_measurement(dl, x, ids, hip, sptr, min(K, 20))
-            if cfg.wdtype == "mxfp4" and cfg.D % 128 == 0 and cfg.I % 128 == 0 else None)
+    tail = w4a8 = decode = None
+    copy_gbs = None
+    if not args.gemm_only:
+        tail = tail_measurement(cfg, hip, sptr, min(K, 50))
+        w4a8 = (w4a8_measurement(dl, x, ids, hip, sptr, min(K, 20))
+                if cfg.wdtype == "mxfp4" and D % 128 == 0 and I % 128 == 0 else None)
+        dT = [int(t) for t in args.decode_T.split(",") if t.strip()]
+        if dT and (D, E, k, I, Is, cfg.wdtype, cfg.route) == (7168, 256, 8, 2048, 2048, "bf16",
+                                                               "sigmoid"):
+            decode = decode_sweep(cfg, layers[0], hip, sptr, dT, 100)
+        copy_gbs = stream_copy_gbs(hip, sptr)
+        print("[bench] tail / decode / copy timed", file=sys.stderr, flush=True)
 
     # algorithmic work of the gate/up SwiGLU GEMM launch (routed + shared groups)
-    T, D, E, k, I, Is = cfg.T, cfg.D, cfg.E, cfg.k, cfg.I, cfg.I_shared
-    R = T * k
-    es = 4 if cfg.act == "f32" else 2
     if cfg.wdtype == "mxfp4":
         w_gu = U * 2 * I * (D // 2 + D // 32)
     else:
@@ -383,17 +603,20 @@ def main():
     gu_bytes = w_gu + T * D * es + (R * I + T * Is) * es
     gu_flops = 4 * R * D * I + 4 * T * D * Is
     achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
-    traffic = measured_traffic(gu_bytes)
+    mfma_peak = (FP8_PEAK_TFLOPS if args.w4a8 else
+                 FP32_PEAK_TFLOPS if cfg.act == "f32" else BF16_PEAK_TFLOPS)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic, "kernel": "k_grouped_gemm_bf16 (gate/up + SwiGLU)",
+                "traffic": measured_traffic(cfg),
+                "kernel": "k_grouped_gemm_bf16 (gate/up + SwiGLU)",
                 "alg_bytes_per_launch": int(gu_bytes),
                 "avg_launch_ms": round(gu_ms, 5),
                 "mfma_tflops": round(gu_flops / (gu_ms * 1e-3) / 1e12, 2),
-                "mfma_frac": round(gu_flops / (gu_ms * 1e-3) / 1e12 /
-                                   (FP8_PEAK_TFLOPS if args.w4a8 else BF16_PEAK_TFLOPS), 4)}
-    if cfg.act == "f32":
-        roofline["bound"] = "hbm"
+                "mfma_peak_tflops": mfma_peak,
+                "mfma_frac": round(gu_flops / (gu_ms * 1e-3) / 1e12 / mfma_peak, 4),
+                "hbm_time_floor_ms": round(gu_bytes / HBM_PEAK_GBS / 1e6, 4),
+                "mfma_time_floor_ms": round(gu_flops / mfma_peak / 1e9, 4),
+                "achievable_copy_gbs": copy_gbs}
 
     # whole-layer algorithmic traffic (touched experts once, shared, router, x, y)
     layer_w = w_gu * 3 // 2 if cfg.wdtype != "mxfp4" else U * 3 * I * (D // 2 + D // 32) + 3 * Is * D * es
@@ -402,40 +625,37 @@ def main():
 
     # CPU oracle on the host cores (bounded sample of the same workload)
     cpu = None
-    if args.cpu_seconds > 0:
+    if cpu_on:
         import oracle
-        xs = synth.x_tokens(cfg)
-        idsn = synth.token_ids(cfg) if cfg.route == "hash" else None
-        T_s = cfg.T
-        if cfg.D * cfg.I * cfg.k > 1 << 26:  # large layers: a 16-token slice
-            T_s = min(16, cfg.T)
-            xs = np.ascontiguousarray(xs[:T_s])
-            idsn = None if idsn is None else np.ascontiguousarray(idsn[:T_s])
-        lg_idx = None
-        experts = {}
-        if cfg.route == "hash":
-            lg_idx, _ = oracle.route(None, None, idsn, T_s, E, k, "hash")
-        else:
-            lg = oracle.router_logits(xs, synth.router_weight(cfg))
-            lg_idx, _ = oracle.route(lg, synth.router_bias(cfg), None, T_s, E, k, cfg.route)
-        for e in np.unique(lg_idx):
-            experts[int(e)] = synth.expert_matrices(cfg, int(e))
-        wr = synth.router_weight(cfg) if cfg.route != "hash" else None
-        bias = synth.router_bias(cfg)
+        T_s, xs, idsn, wr_h, bias_h, need = sample
+        experts = dl.host_experts
         sh = synth.shared_matrices(cfg)
+        run = lambda n: oracle.layer_forward(
+            np.ascontiguousarray(xs[:n]), None if idsn is None else np.ascontiguousarray(idsn[:n]),
+            wr_h, bias_h, experts, sh, n, D, E, k, I, Is, cfg.route, cfg.wdtype, glu=args.glu)
+        nthr = oracle.num_threads()
         runs, t_cpu = 0, 0.0
         while runs == 0 or t_cpu < args.cpu_seconds:
             c0 = time.perf_counter()
-            oracle.layer_forward(xs, idsn, wr, bias, experts, sh, T_s, D, E, k, I,
-                                 Is, cfg.route, cfg.wdtype, glu=args.glu)
+            run(T_s)
             t_cpu += time.perf_counter() - c0
             runs += 1
+        # one token on one thread
+        oracle.set_num_threads(1)
+        c0 = time.perf_counter()
+        run(1)
+        t1 = time.perf_counter() - c0
+        oracle.set_num_threads(nthr)
         cpu = {"value": round(runs * T_s / t_cpu, 2), "unit": "tokens/s",
-               "cores": oracle.num_threads(), "kind": "oracle",
-               "sample": f"{runs} x oracle layer forward of {T_s} tokens of the same recipe "
-                         f"({t_cpu:.1f} s)"}
+               "cores": nthr, "kind": "oracle",
+               "sample": f"{runs} x oracle layer forward of the batch's first {T_s} tokens "
+                         f"({t_cpu:.1f} s; the experts those tokens route to, the shared "
+                         f"expert and the router)",
+               "single_thread_tokens_per_s": round(1.0 / t1, 3),
+               **cpu_info()}
 
-    tokens_per_s = cfg.T / (ms_per_step * 1e-3)
+    tokens_per_s = T / (ms_per_step * 1e-3)
+    nz = counts[counts > 0]
     out = {
         "metric": "MoE-layer tokens/s; %MFMA peak (prefill), %HBM GB/s (decode)",
         "value": round(tokens_per_s, 1),
@@ -459,11 +679,19 @@ def main():
                    "activation_format": "mxfp8" if args.w4a8 else cfg.act,
                    "parallelism": "single GPU",
                    "weight_replicas": nrep, "experts_touched": U,
+                   "zero_load_experts": int(E - U),
+                   "mean_rows_per_expert": round(float(R) / E, 2),
+                   "mean_rows_per_touched_expert": round(float(nz.mean()), 2) if U else 0.0,
                    "max_rows_per_expert": int(counts.max())},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "step_ms": {"p10": round(float(np.percentile(step_ms, 10)), 5),
+                    "p50": round(float(np.percentile(step_ms, 50)), 5),
+                    "p90": round(float(np.percentile(step_ms, 90)), 5)},
+        "clocks": clocks.summary(),
         "tail": tail,
         "w4a8": w4a8,
+        "decode": decode,
         "layer": {"alg_bytes": int(layer_bytes), "flops": int(layer_flops),
                   "gbs": round(layer_bytes / (ms_per_step * 1e-3) / 1e9, 1),
                   "hbm_frac": round(layer_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -472,6 +700,7 @@ def main():
                   "kernel_ms": {"gate_up_gemm": round(float(kern_ms[0]), 5),
                                 "down_gemm": round(float(kern_ms[1]), 5)},
                   "gpu_event_ms_per_step": round(gpu_ms / K, 5)},
+        "build_id": moe.build_id(),
     }
     print(json.dumps(out), flush=True)
 
