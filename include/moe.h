@@ -307,6 +307,31 @@ int moe_layer_forward(const void* x, const int32_t* token_ids, const void* w_rou
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * moe_layer_forward_noalloc — moe_layer_forward for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The caller passes inputs and outputs only;
+ * the workspace is a scratch array of MOE_NOALLOC_SCRATCH_BYTES that the
+ * library holds in device memory, one copy per GPU, kept until the process
+ * ends.  Arguments, results and bits are those of moe_layer_forward (the
+ * same kernels).  The call allocates nothing and calls no allocating library
+ * routine; its first call on a device looks up that device's scratch address.
+ *  Limit: moe_layer_workspace_bytes(T, D, E, k, I, I_shared, act, routed
+ *  dtype) must not exceed MOE_NOALLOC_SCRATCH_BYTES (64 MiB: decode batches of
+ *  a D = 7168, E = 256, k = 8, I = 2048 layer up to a few hundred tokens);
+ *  larger layers get MOE_ERR_WORKSPACE before anything is launched.
+ *  Every call on one GPU uses the same scratch, which keeps the last call's
+ *  contents (each call writes what it reads first).  Calls that overlap on
+ *  one GPU (two streams, or two host threads without ordering) race on it:
+ *  order them on one stream.
+ * ------------------------------------------------------------------------- */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int moe_layer_forward_noalloc(const void* x, const int32_t* token_ids, const void* w_router,
+                              const float* bias, const moe_expert_weights* routed,
+                              const moe_expert_weights* shared, int64_t T, int D, int E, int k,
+                              int I, int I_shared, moe_route mode, moe_dtype act,
+                              uint32_t flags, void* y, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Stage timing (measurement only).  When set, the next moe_layer_forward
  * calls on this host thread record events[0] before the first kernel and
  * events[i+1] after stage i on the call's stream; stages: 0 routing,

@@ -32,7 +32,7 @@ EXPORTS = ("moe_router_workspace_bytes", "moe_router_topk", "moe_routing_scores"
            "moe_combine", "moe_residual_rmsnorm", "moe_combine_rmsnorm",
            "moe_layer_workspace_bytes", "moe_layer_forward",
            "moe_set_stage_events", "moe_status_string", "moe_last_error", "moe_abi_version",
-           "moe_build_id")
+           "moe_build_id", "moe_layer_forward_noalloc")
 
 
 class MoEError(RuntimeError):
@@ -82,6 +82,8 @@ def lib() -> ctypes.CDLL:
         L.moe_layer_workspace_bytes.restype = sz
         L.moe_layer_forward.argtypes = [vp, vp, vp, vp, WP, WP, i64, i32, i32, i32, i32, i32, i32,
                                         i32, u32, vp, vp, sz, vp]
+        L.moe_layer_forward_noalloc.argtypes = [vp, vp, vp, vp, WP, WP, i64, i32, i32, i32, i32,
+                                                i32, i32, i32, u32, vp, vp]
         L.moe_set_stage_events.argtypes = [vp, i32]
         L.moe_status_string.argtypes = [i32]
         L.moe_status_string.restype = ctypes.c_char_p
@@ -90,6 +92,7 @@ def lib() -> ctypes.CDLL:
         for name in ("moe_router_topk", "moe_routing_scores", "moe_permute", "moe_grouped_swiglu", "moe_combine",
                      "moe_residual_rmsnorm", "moe_combine_rmsnorm", "moe_layer_forward",
                      "moe_mx_e4m3_quantize", "moe_grouped_swiglu_w4a8",
+                     "moe_layer_forward_noalloc",
                      "moe_set_stage_events", "moe_abi_version"):
             getattr(L, name).restype = i32
         _lib = L
@@ -379,6 +382,30 @@ def layer_forward(x, token_ids, w_router, bias, routed: ExpertWeights,
                                T, D, E, k, I, Is, ROUTE[mode], act,
                                GLU[glu] | (FLAG_W4A8 if w4a8 else 0), _ptr(out), ws_ptr,
                                ws_bytes, _stream(stream)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES
+
+
+@_allocating
+def layer_forward_noalloc(x, token_ids, w_router, bias, routed: ExpertWeights,
+                          shared: Optional[ExpertWeights], E: int, k: int, mode: str, out=None,
+                          stream=None, glu: str = "swiglu", w4a8: bool = False):
+    """layer_forward on the library's fixed device scratch (no workspace
+    argument; moe_layer_forward_noalloc).  Pass `out` to allocate nothing at
+    all.  Calls that overlap on one GPU race on the scratch."""
+    T, D = x.shape
+    I = routed.gate.shape[1]
+    Is = shared.gate.shape[1] if shared is not None else 0
+    if out is None:
+        out = torch.empty((T, D), dtype=x.dtype, device=x.device)
+    r = routed.as_struct()
+    s = shared.as_struct() if shared is not None else None
+    _check(lib().moe_layer_forward_noalloc(
+        _ptr(x), _ptr(token_ids), _ptr(w_router), _ptr(bias), ctypes.byref(r),
+        ctypes.byref(s) if s is not None else None, T, D, E, k, I, Is, ROUTE[mode], _act(x),
+        GLU[glu] | (FLAG_W4A8 if w4a8 else 0), _ptr(out), _stream(stream)))
     return out
 
 

@@ -27,7 +27,8 @@ DEVICE_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-result",
 ]
-SOURCES = ["router.hip", "permute.hip", "gemm.hip", "combine.hip", "quant.hip", "abi.cpp"]
+SOURCES = ["router.hip", "permute.hip", "gemm.hip", "combine.hip", "quant.hip", "noalloc.hip",
+           "abi.cpp"]
 HEADER = os.path.join(os.path.dirname(PKG), "include", "moe.h")
 
 

@@ -274,6 +274,16 @@ moe::GemmSeg make_seg(const void* A, const int32_t* a_index, const int32_t* offs
 
 }  // namespace
 
+namespace moe {
+int set_error(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+}  // namespace moe
+
 extern "C" {
 
 int moe_abi_version(void) { return MOE_ABI_VERSION; }

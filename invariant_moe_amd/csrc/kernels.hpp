@@ -8,6 +8,10 @@
 
 namespace moe {
 
+// Sets the thread-local message that moe_last_error() returns (printf
+// format) and returns status.
+int set_error(int status, const char* fmt, ...);
+
 // One segment of a grouped GEMM: G groups of rows that share the reduction
 // input layout; group g uses weights [g] of W0/W1 (and scales S0/S1).
 struct GemmSeg {
