@@ -369,6 +369,20 @@ def stream_copy_gbs(hip, sptr, nbytes=4 << 30, reps=10):
     return round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
 
 
+def _time_steps(hip, sptr, fn, n, warm=5):
+    import torch
+    for i in range(warm):
+        fn(i)
+    e0, e1 = hip.event(), hip.event()
+    torch.cuda.synchronize()
+    hip.record(e0, sptr)
+    for i in range(n):
+        fn(i)
+    hip.record(e1, sptr)
+    torch.cuda.synchronize()
+    return hip.elapsed_ms(e0, e1) / n
+
+
 def decode_sweep(cfg3, layer, hip, sptr, Ts, steps: int):
     """The DeepSeek-V3-shaped layer at decode batch sizes on the resident
     weights: the 64-token decode pool (seeded), one window of T tokens per step,
@@ -396,24 +410,38 @@ def decode_sweep(cfg3, layer, hip, sptr, Ts, steps: int):
             U.append(int(torch.unique(idx).numel()))
             xs.append(x)
         y = torch.empty((T, D), dtype=torch.bfloat16, device="cuda")
-        for i in range(5):
-            layer.forward(xs[i % nwin], out=y)
-        e0, e1 = hip.event(), hip.event()
-        torch.cuda.synchronize()
-        hip.record(e0, sptr)
-        for i in range(steps):
-            layer.forward(xs[i % nwin], out=y)
-        hip.record(e1, sptr)
-        torch.cuda.synchronize()
-        ms = hip.elapsed_ms(e0, e1) / steps
+        ms = _time_steps(hip, sptr, lambda i: layer.forward(xs[i % nwin], out=y), steps)
+        fws = moe.fused_workspace(T, D, E, k, I, Is, "cuda")
+        ms_f = _time_steps(hip, sptr, lambda i: moe.layer_forward_fused(
+            xs[i % nwin], None, layer.w_router, layer.bias, layer.routed, layer.shared, E, k,
+            "sigmoid", out=y, workspace=fws), steps)
+        if moe.fused_error(fws):
+            raise RuntimeError("single-launch forward: a bounded wait gave up")
         u = float(np.mean([U[i % nwin] for i in range(steps)]))
         nbytes = u * 3 * I * D * 2 + 3 * Is * D * 2 + E * D * 2 + E * 4 + 2 * T * D * 2
         gbs = nbytes / (ms * 1e-3) / 1e9
+        gbs_f = nbytes / (ms_f * 1e-3) / 1e9
         res.append({"T": T, "ms": round(ms, 5), "experts_touched": round(u, 2),
                     "alg_bytes": int(nbytes), "gbs": round(gbs, 1),
                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-                    "tokens_per_s": round(T / (ms * 1e-3), 1)})
+                    "tokens_per_s": round(T / (ms * 1e-3), 1),
+                    "fused_ms": round(ms_f, 5), "fused_hbm_frac": round(gbs_f / HBM_PEAK_GBS, 4)})
     return res
+
+
+def fused_layer_ms(layer, x, ids, hip, sptr, steps: int):
+    """The same layer step in one kernel launch (moe_layer_forward_fused)."""
+    import invariant_moe_amd as moe
+    T, D = x.shape
+    I, Is = layer.routed.gate.shape[1], (layer.shared.gate.shape[1] if layer.shared else 0)
+    fws = moe.fused_workspace(T, D, layer.E, layer.k, I, Is, "cuda")
+    y = x.new_empty((T, D))
+    ms = _time_steps(hip, sptr, lambda i: moe.layer_forward_fused(
+        x, ids, layer.w_router, layer.bias, layer.routed, layer.shared, layer.E, layer.k,
+        layer.mode, out=y, workspace=fws, glu=layer.glu), steps)
+    if moe.fused_error(fws):
+        raise RuntimeError("single-launch forward: a bounded wait gave up")
+    return ms
 
 
 def cpu_info():
@@ -581,9 +609,14 @@ def main():
     gu_ms = float(kern_ms[0])
     print("[bench] layer timed", file=sys.stderr, flush=True)
 
-    tail = w4a8 = decode = None
+    tail = w4a8 = decode = fused = None
     copy_gbs = None
     if not args.gemm_only:
+        if cfg.act == "bf16" and not args.w4a8:
+            fms = fused_layer_ms(layers[0], x, ids, hip, sptr, min(K, 50))
+            fused = {"ms_per_step": round(fms, 5), "tokens_per_s": round(T / (fms * 1e-3), 1),
+                     "kernel": "k_layer_fused (one launch: routing, permutation, both GEMMs, "
+                               "combine)"}
         tail = tail_measurement(cfg, hip, sptr, min(K, 50))
         w4a8 = (w4a8_measurement(dl, x, ids, hip, sptr, min(K, 20))
                 if cfg.wdtype == "mxfp4" and D % 128 == 0 and I % 128 == 0 else None)
@@ -692,6 +725,7 @@ def main():
         "tail": tail,
         "w4a8": w4a8,
         "decode": decode,
+        "fused": fused,
         "layer": {"alg_bytes": int(layer_bytes), "flops": int(layer_flops),
                   "gbs": round(layer_bytes / (ms_per_step * 1e-3) / 1e9, 1),
                   "hbm_frac": round(layer_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

@@ -307,6 +307,36 @@ int moe_layer_forward(const void* x, const int32_t* token_ids, const void* w_rou
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * moe_layer_forward_fused — the whole layer in ONE kernel launch ([DS] 6.1:
+ * dispatch, expert compute and combine fused into one kernel whose experts
+ * are processed in waves).  Same arguments, results and bits as
+ * moe_layer_forward: every step runs the same fixed chains (router order,
+ * top-k, counting sort, one MFMA chain per GEMM output, fixed-order combine);
+ * only the GEMM tile shapes may differ, which changes no bit.
+ *  The launch's workgroups draw the layer's steps as tasks from one ordered
+ *  queue (router logits, shared-expert gate/up, top-k, permutation, routed
+ *  gate/up, shared down, routed down, combine); a task waits only for whole
+ *  earlier phases, so the shared expert's gate/up overlaps the routing and no
+ *  kernel boundary separates the steps.
+ *  Limits: act = MOE_BF16; routed weights MOE_BF16 or MOE_MXFP4; the shared
+ *  expert (if any) MOE_BF16; flags 0, MOE_FLAG_GLU_CLAMP or MOE_FLAG_GLU_SITU
+ *  (MOE_FLAG_W4A8 gives MOE_ERR_UNSUPPORTED).
+ *  workspace: moe_layer_fused_workspace_bytes(...) bytes, 256-byte aligned.
+ *  Its first 256 bytes hold the task queue's state: they must be zero before
+ *  the first call on that workspace (e.g. the workspace allocated zeroed),
+ *  and every call leaves them zero again.  The 32-bit word at byte offset 8 is
+ *  a sticky error flag: nonzero if a wait inside a call gave up (a bounded
+ *  spin; the outputs of that call are then undefined).  Calls that share a
+ *  workspace must be ordered (one stream).
+ * ------------------------------------------------------------------------- */
+size_t moe_layer_fused_workspace_bytes(int64_t T, int D, int E, int k, int I, int I_shared);
+int moe_layer_forward_fused(const void* x, const int32_t* token_ids, const void* w_router,
+                            const float* bias, const moe_expert_weights* routed,
+                            const moe_expert_weights* shared, int64_t T, int D, int E, int k,
+                            int I, int I_shared, moe_route mode, moe_dtype act, uint32_t flags,
+                            void* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * moe_layer_forward_noalloc — moe_layer_forward for callers that cannot
  * allocate device memory: code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc.  The caller passes inputs and outputs only;

@@ -32,7 +32,8 @@ EXPORTS = ("moe_router_workspace_bytes", "moe_router_topk", "moe_routing_scores"
            "moe_combine", "moe_residual_rmsnorm", "moe_combine_rmsnorm",
            "moe_layer_workspace_bytes", "moe_layer_forward",
            "moe_set_stage_events", "moe_status_string", "moe_last_error", "moe_abi_version",
-           "moe_build_id", "moe_layer_forward_noalloc")
+           "moe_build_id", "moe_layer_forward_noalloc", "moe_layer_fused_workspace_bytes",
+           "moe_layer_forward_fused")
 
 
 class MoEError(RuntimeError):
@@ -84,6 +85,10 @@ def lib() -> ctypes.CDLL:
                                         i32, u32, vp, vp, sz, vp]
         L.moe_layer_forward_noalloc.argtypes = [vp, vp, vp, vp, WP, WP, i64, i32, i32, i32, i32,
                                                 i32, i32, i32, u32, vp, vp]
+        L.moe_layer_fused_workspace_bytes.argtypes = [i64, i32, i32, i32, i32, i32]
+        L.moe_layer_fused_workspace_bytes.restype = sz
+        L.moe_layer_forward_fused.argtypes = [vp, vp, vp, vp, WP, WP, i64, i32, i32, i32, i32, i32,
+                                              i32, i32, u32, vp, vp, sz, vp]
         L.moe_set_stage_events.argtypes = [vp, i32]
         L.moe_status_string.argtypes = [i32]
         L.moe_status_string.restype = ctypes.c_char_p
@@ -92,7 +97,7 @@ def lib() -> ctypes.CDLL:
         for name in ("moe_router_topk", "moe_routing_scores", "moe_permute", "moe_grouped_swiglu", "moe_combine",
                      "moe_residual_rmsnorm", "moe_combine_rmsnorm", "moe_layer_forward",
                      "moe_mx_e4m3_quantize", "moe_grouped_swiglu_w4a8",
-                     "moe_layer_forward_noalloc",
+                     "moe_layer_forward_noalloc", "moe_layer_forward_fused",
                      "moe_set_stage_events", "moe_abi_version"):
             getattr(L, name).restype = i32
         _lib = L
@@ -385,6 +390,52 @@ def layer_forward(x, token_ids, w_router, bias, routed: ExpertWeights,
     return out
 
 
+def fused_workspace(T, D, E, k, I, I_shared, device) -> torch.Tensor:
+    """A workspace for layer_forward_fused: zeroed (the task queue's header must
+    start at zero), with room to align it to 256 bytes."""
+    nb = lib().moe_layer_fused_workspace_bytes(T, D, E, k, I, I_shared)
+    return torch.zeros(int(nb) + 256, dtype=torch.uint8, device=device)
+
+
+def _aligned(ws: torch.Tensor):
+    p = (ws.data_ptr() + 255) // 256 * 256
+    return p, ws.numel() - (p - ws.data_ptr())
+
+
+def fused_error(workspace: torch.Tensor) -> int:
+    """The sticky error word of a fused workspace (nonzero: a bounded wait gave
+    up in some call).  Synchronises with the device."""
+    p, _ = _aligned(workspace)
+    off = p - workspace.data_ptr()
+    return int(workspace[off + 8:off + 12].cpu().view(torch.int32)[0])
+
+
+@_allocating
+def layer_forward_fused(x, token_ids, w_router, bias, routed: ExpertWeights,
+                        shared: Optional[ExpertWeights], E: int, k: int, mode: str, out=None,
+                        workspace=None, stream=None, glu: str = "swiglu"):
+    """The whole layer in one kernel launch (moe_layer_forward_fused): y [T, D],
+    bit-identical to layer_forward.  workspace: from fused_workspace (zeroed);
+    reuse it across calls on one stream."""
+    T, D = x.shape
+    I = routed.gate.shape[1]
+    Is = shared.gate.shape[1] if shared is not None else 0
+    L = lib()
+    nb = L.moe_layer_fused_workspace_bytes(T, D, E, k, I, Is)
+    if workspace is None or workspace.numel() < nb + 256:
+        workspace = fused_workspace(T, D, E, k, I, Is, x.device)
+    if out is None:
+        out = torch.empty((T, D), dtype=x.dtype, device=x.device)
+    ws_ptr, ws_bytes = _aligned(workspace)
+    r = routed.as_struct()
+    s = shared.as_struct() if shared is not None else None
+    _check(L.moe_layer_forward_fused(_ptr(x), _ptr(token_ids), _ptr(w_router), _ptr(bias),
+                                     ctypes.byref(r), ctypes.byref(s) if s is not None else None,
+                                     T, D, E, k, I, Is, ROUTE[mode], _act(x), GLU[glu],
+                                     _ptr(out), ws_ptr, ws_bytes, _stream(stream)))
+    return out
+
+
 NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES
 
 
@@ -430,22 +481,33 @@ class MoELayer:
     with it (the allocator reuses a block only after its stream's work)."""
 
     def __init__(self, w_router, bias, routed: ExpertWeights, shared: Optional[ExpertWeights],
-                 E: int, k: int, mode: str, glu: str = "swiglu", w4a8: bool = False):
+                 E: int, k: int, mode: str, glu: str = "swiglu", w4a8: bool = False,
+                 fused: bool = False):
         self.w_router, self.bias, self.routed, self.shared = w_router, bias, routed, shared
         self.E, self.k, self.mode, self.glu, self.w4a8 = E, k, mode, glu, w4a8
+        self.fused = fused  # one kernel launch per forward (layer_forward_fused)
         self._ws = {}  # stream handle -> workspace allocated on that stream
 
     def forward(self, x, token_ids=None, out=None, stream=None):
         T, D = x.shape
         I = self.routed.gate.shape[1]
         Is = self.shared.gate.shape[1] if self.shared is not None else 0
-        nb = layer_workspace_bytes(T, D, self.E, self.k, I, Is, _act(x), self.routed.dtype) + 256
         st = stream if stream is not None else torch.cuda.current_stream()
+        if self.fused:
+            nb = lib().moe_layer_fused_workspace_bytes(T, D, self.E, self.k, I, Is) + 256
+        else:
+            nb = layer_workspace_bytes(T, D, self.E, self.k, I, Is, _act(x),
+                                       self.routed.dtype) + 256
         ws = self._ws.get(st.cuda_stream)
         if ws is None or ws.numel() < nb:
             with _on(st):
-                ws = _workspace(nb, x.device)
+                ws = (fused_workspace(T, D, self.E, self.k, I, Is, x.device) if self.fused
+                      else _workspace(nb, x.device))
             self._ws[st.cuda_stream] = ws
+        if self.fused:
+            return layer_forward_fused(x, token_ids, self.w_router, self.bias, self.routed,
+                                       self.shared, self.E, self.k, self.mode, out=out,
+                                       workspace=ws, stream=st, glu=self.glu)
         return layer_forward(x, token_ids, self.w_router, self.bias, self.routed, self.shared,
                              self.E, self.k, self.mode, out=out, workspace=ws,
                              stream=st, glu=self.glu, w4a8=self.w4a8)

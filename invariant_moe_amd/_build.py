@@ -28,6 +28,7 @@ DEVICE_FLAGS = [
     "-Wall", "-Wno-unused-result",
 ]
 SOURCES = ["router.hip", "permute.hip", "gemm.hip", "combine.hip", "quant.hip", "noalloc.hip",
+           "fused.hip",
            "abi.cpp"]
 HEADER = os.path.join(os.path.dirname(PKG), "include", "moe.h")
 

@@ -798,3 +798,202 @@ int moe_layer_forward(const void* x, const int32_t* token_ids, const void* w_rou
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Single-launch layer forward
+// ---------------------------------------------------------------------------
+static int64_t round8(int64_t v) { return (v + 7) / 8 * 8; }
+
+// Table entries of a routed GEMM with row tile BM and feature tile BN (the
+// bound the unfused planner uses: every non-empty group may add one partial
+// row tile).
+static int64_t routed_tile_bound(int64_t R, int E, int N, int BM, int BN) {
+  const int64_t nonempty = R < E ? R : E;
+  return round8(((R + BM - 1) / BM + nonempty) * ((N + BN - 1) / BN));
+}
+
+struct FusedLayout {
+  LayerLayout L;   // offsets relative to `layer`
+  size_t layer, tab_gu, tab_dn, row_done, total;
+  int64_t n_gu, n_dn;
+};
+
+// Queue header, the layer's workspace, then the two routed tile tables (sized
+// for either routed weight format).
+static FusedLayout fused_layout(int64_t T, int D, int E, int k, int I, int Is) {
+  FusedLayout f{};
+  const int64_t R = T * k;
+  Carver c;
+  c.take(moe::kFusedHdrBytes);
+  f.L = layer_layout(T, D, E, k, I, Is, MOE_BF16);
+  f.layer = c.take(f.L.total);
+  for (int fp4 = 0; fp4 < 2; ++fp4) {
+    int BM, BNg, BNd;
+    moe::fused_tiles(moe::fused_cfg(R / E, fp4 != 0), &BM, &BNg, &BNd);
+    f.n_gu = std::max(f.n_gu, routed_tile_bound(R, E, I, BM, BNg));
+    f.n_dn = std::max(f.n_dn, routed_tile_bound(R, E, D, BM, BNd));
+  }
+  f.tab_gu = c.take((size_t)f.n_gu * sizeof(int4));
+  f.tab_dn = c.take((size_t)f.n_dn * sizeof(int4));
+  f.row_done = c.take((size_t)R * 4);
+  f.total = c.off;
+  return f;
+}
+
+extern "C" {
+
+size_t moe_layer_fused_workspace_bytes(int64_t T, int D, int E, int k, int I, int I_shared) {
+  if (T < 0 || D <= 0 || E <= 0 || k <= 0 || I <= 0) return 0;
+  return fused_layout(T, D, E, k, I, I_shared > 0 ? I_shared : 0).total;
+}
+
+int moe_layer_forward_fused(const void* x, const int32_t* token_ids, const void* w_router,
+                            const float* bias, const moe_expert_weights* routed,
+                            const moe_expert_weights* shared, int64_t T, int D, int E, int k,
+                            int I, int I_shared, moe_route mode, moe_dtype act, uint32_t flags,
+                            void* y, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc;
+  if (act != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "the single-launch forward runs bf16 activations only");
+  if ((rc = check_dims(T, D, E, k))) return rc;
+  int glu;
+  if (flags & MOE_FLAG_W4A8)
+    return fail(MOE_ERR_UNSUPPORTED, "the single-launch forward does not run MOE_FLAG_W4A8");
+  if ((rc = glu_from_flags(flags, &glu))) return rc;
+  if (I < 32 || I % 32) return fail(MOE_ERR_SHAPE, "I=%d must be a positive multiple of 32", I);
+  if (mode != MOE_ROUTE_SOFTMAX && mode != MOE_ROUTE_SIGMOID && mode != MOE_ROUTE_HASH)
+    return fail(MOE_ERR_SHAPE, "unknown routing mode %d", (int)mode);
+  if ((rc = check_weights(routed, act, "routed"))) return rc;
+  const int Is = shared ? I_shared : 0;
+  if (shared) {
+    if ((rc = check_weights(shared, act, "shared"))) return rc;
+    if (shared->dtype != MOE_BF16)
+      return fail(MOE_ERR_UNSUPPORTED, "the single-launch forward runs a bf16 shared expert");
+    if (Is < 32 || Is % 32)
+      return fail(MOE_ERR_SHAPE, "I_shared=%d must be a positive multiple of 32", I_shared);
+  }
+  if (T > 0 && (!x || !y)) return fail(MOE_ERR_NULL, "x / y are NULL");
+  if (T > 0 && (!aligned(x, 16) || !aligned(y, 16)))
+    return fail(MOE_ERR_ALIGN, "x / y must be 16-byte aligned");
+  if (mode == MOE_ROUTE_HASH) {
+    if (!token_ids) return fail(MOE_ERR_NULL, "hash routing needs token_ids");
+  } else {
+    if (!w_router) return fail(MOE_ERR_NULL, "w_router is NULL");
+    if (!aligned(w_router, 16)) return fail(MOE_ERR_ALIGN, "w_router must be 16-byte aligned");
+    if (bias && !aligned(bias, 4)) return fail(MOE_ERR_ALIGN, "bias misaligned");
+  }
+  const FusedLayout F = fused_layout(T, D, E, k, I, Is);
+  if (!workspace || workspace_bytes < F.total)
+    return fail(MOE_ERR_WORKSPACE, "fused layer workspace needs %zu bytes", F.total);
+  if (!aligned(workspace, 256)) return fail(MOE_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if (T == 0) return ok();
+
+  const bool fp4 = routed->dtype == MOE_MXFP4;
+  const int64_t R = T * k, W = (T + 63) / 64;
+  const int cfg = moe::fused_cfg(R / E, fp4);
+  int BM, BNg, BNd;
+  moe::fused_tiles(cfg, &BM, &BNg, &BNd);
+  char* ws = static_cast<char*>(workspace);
+  char* lw = ws + F.layer;
+  const LayerLayout& L = F.L;
+
+  moe::FusedArgs a{};
+  a.hdr = reinterpret_cast<moe::FusedHdr*>(ws);
+  a.x = static_cast<const uint16_t*>(x);
+  a.token_ids = token_ids;
+  a.w_router = static_cast<const uint16_t*>(w_router);
+  a.bias = bias;
+  a.T = T;
+  a.D = D;
+  a.E = E;
+  a.k = k;
+  a.mode = (int)mode;
+  a.logits = reinterpret_cast<float*>(lw + L.logits);
+  a.idx = reinterpret_cast<int32_t*>(lw + L.idx);
+  a.tw = reinterpret_cast<float*>(lw + L.w);
+  a.mask = reinterpret_cast<uint64_t*>(lw + L.mask);
+  a.W = W;
+  a.wprefix = reinterpret_cast<int32_t*>(lw + L.wprefix);
+  a.counts = reinterpret_cast<int32_t*>(lw + L.counts);
+  a.offsets = reinterpret_cast<int32_t*>(lw + L.offsets);
+  a.row_token = reinterpret_cast<int32_t*>(lw + L.row_token);
+  a.pair_row = reinterpret_cast<int32_t*>(lw + L.pair_row);
+  void* h = lw + L.h;
+  void* hs = lw + L.hs;
+  void* o = lw + L.o;
+  void* sh = lw + L.s;
+  int4* tab_gu = reinterpret_cast<int4*>(ws + F.tab_gu);
+  int4* tab_dn = reinterpret_cast<int4*>(ws + F.tab_dn);
+  a.tab_gu = tab_gu;
+  a.tab_dn = tab_dn;
+  a.row_done = reinterpret_cast<unsigned*>(ws + F.row_done);
+  a.gu_ntiles = (I + BNg - 1) / BNg;
+  a.glu = glu;
+
+  int64_t n[moe::FP_COUNT] = {};
+  // routing: logit tiles as the router kernels choose them by T, or hash blocks
+  if (mode == MOE_ROUTE_HASH) {
+    a.route_var = 3;
+    n[moe::FP_ROUTE] = W;
+  } else {
+    int TT, EXP;  // tokens and experts per logit tile
+    if (T < 16) { a.route_var = 0; TT = 1; EXP = 4; }
+    else if (T <= 128) { a.route_var = 1; TT = 4; EXP = 8; }
+    else { a.route_var = 2; TT = 16; EXP = 16; }
+    a.route_gy = (E + EXP - 1) / EXP;
+    n[moe::FP_ROUTE] = (T + TT - 1) / TT * a.route_gy;
+    a.n_zero = (int64_t)E * W;
+    n[moe::FP_TOPK] = (T + 3) / 4;
+    int c = 1;
+    while (c * 64 < E) c *= 2;
+    a.topk_c = c;
+  }
+  // permutation and the routed tile tables
+  moe::TileJobs jobs{};
+  jobs.n = 2;
+  jobs.BM = BM;
+  const int64_t n_gu = routed_tile_bound(R, E, I, BM, BNg), n_dn = routed_tile_bound(R, E, D, BM, BNd);
+  if (n_gu > F.n_gu || n_dn > F.n_dn)
+    return fail(MOE_ERR_WORKSPACE, "tile tables exceed their workspace region");
+  jobs.job[0] = moe::TileJob{tab_gu, n_gu, BM, BNg, 1, {1, 0}, {R, 0}, {I, 0}};
+  jobs.job[1] = moe::TileJob{tab_dn, n_dn, BM, BNd, 1, {1, 0}, {R, 0}, {D, 0}};
+  a.jobs = jobs;
+  int64_t nperm = std::max((R + 1023) / 1024, (n_gu + n_dn + 511) / 512);
+  a.n_perm = (int)std::min<int64_t>(std::max<int64_t>(nperm, 1), 64);
+  n[moe::FP_PERM] = a.n_perm;
+  n[moe::FP_GU] = n_gu;
+  n[moe::FP_DN] = n_dn;
+  // expert GEMM segments (routed rows gathered through row_token)
+  a.gu_r = make_seg(x, a.row_token, a.offsets, R, E, D, I, routed, true, h);
+  a.dn_r = make_seg(h, nullptr, a.offsets, R, E, I, D, routed, false, o);
+  if (shared) {
+    a.gu_s = make_seg(x, nullptr, nullptr, T, 1, D, Is, shared, true, hs);
+    a.dn_s = make_seg(hs, nullptr, nullptr, T, 1, Is, D, shared, false, sh);
+    a.sh_mt = (int)((T + BM - 1) / BM);
+    n[moe::FP_SGU] = (int64_t)a.sh_mt * ((Is + BNg - 1) / BNg);
+    n[moe::FP_SDN] = (int64_t)a.sh_mt * ((D + BNd - 1) / BNd);
+  }
+  // combine
+  int tpt = 64;
+  while (tpt < 256 && tpt * 8 < D) tpt *= 2;
+  a.comb_tpt = tpt;
+  a.comb_gy = (D / 8 + tpt - 1) / tpt;
+  n[moe::FP_COMB] = (T + (256 / tpt) - 1) / (256 / tpt) * a.comb_gy;
+  a.o = static_cast<const uint16_t*>(o);
+  a.s = shared ? static_cast<const uint16_t*>(sh) : nullptr;
+  a.y = static_cast<uint16_t*>(y);
+
+  int64_t total = 0;
+  for (int p = 0; p < moe::FP_COUNT; ++p) {
+    a.start[p] = (unsigned)total;
+    total += n[p];
+  }
+  if (total >= ((int64_t)1 << 31)) return fail(MOE_ERR_SHAPE, "too many tasks for one launch");
+  a.start[moe::FP_COUNT] = (unsigned)total;
+  const int64_t grid = moe::fused_grid(cfg, fp4, total);
+  if (grid <= 0) return hip_status(hipGetLastError(), "fused occupancy query");
+  return hip_status(moe::launch_layer_fused(a, cfg, fp4, grid, static_cast<hipStream_t>(stream)),
+                    "fused layer");
+}
+
+}  // extern "C"

@@ -32,6 +32,42 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
 }
 
+// Stores of results that other workgroups of the SAME launch read (the
+// single-launch layer kernel): CO = true makes them agent-scope coherent
+// stores, visible to every XCD once they complete, so the producer needs no
+// L2 write-back fence (measured at 9-35 us per fence on MI355X) before it
+// signals; the reader still takes an agent-scope acquire.  CO = false is a
+// plain store (separate kernels: the kernel boundary makes results visible).
+template <bool CO>
+struct Out {
+  template <typename T>
+  __device__ __forceinline__ static void put(T* p, T v) {
+    if constexpr (CO)
+      __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      *p = v;
+  }
+  __device__ __forceinline__ static void put2(uint2* p, uint2 v) {  // 8 bytes
+    if constexpr (CO)
+      __hip_atomic_store(reinterpret_cast<unsigned long long*>(p),
+                         (unsigned long long)v.x | ((unsigned long long)v.y << 32),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      *p = v;
+  }
+  __device__ __forceinline__ static void put4(int4* p, int4 v) {  // 16 bytes, as two halves
+    if constexpr (CO) {
+      unsigned long long* q = reinterpret_cast<unsigned long long*>(p);
+      __hip_atomic_store(q, (unsigned long long)(unsigned)v.x | ((unsigned long long)(unsigned)v.y << 32),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(q + 1, (unsigned long long)(unsigned)v.z | ((unsigned long long)(unsigned)v.w << 32),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      *p = v;
+    }
+  }
+};
+
 // Logical id of a workgroup such that consecutive logical ids run on the same
 // XCD (workgroups are dealt round-robin over the 8 XCDs by blockIdx.x).
 // Returns -1 when this workgroup has no logical id below `total`.

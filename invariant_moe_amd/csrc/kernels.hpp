@@ -129,6 +129,94 @@ bool plan_tile_jobs(const GemmPlan& p, int4* tables, TileJobs& jobs);
 hipError_t launch_grouped_gemm(const GemmPlan& p, const GemmArgs& a, int4* tables, hipStream_t s,
                                hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
+// ---------------------------------------------------------------------------
+// Single-launch layer forward (fused.hip).  One kernel runs every step of the
+// layer as tasks of one ordered queue; a task waits only for tasks of earlier
+// phases (counted per phase), so no wait can block on a workgroup that has not
+// started.
+// ---------------------------------------------------------------------------
+enum FusedPhase {
+  FP_ROUTE = 0,  // router logits (+ clearing the mask words) or hash routing
+  FP_SGU,        // shared expert gate/up tiles (need only x)
+  FP_TOPK,       // top-k + weights, 4 tokens per task
+  FP_PERM,       // permutation + routed tile tables
+  FP_GU,         // routed gate/up tiles (table)
+  FP_SDN,        // shared expert down tiles
+  FP_DN,         // routed down tiles (table)
+  FP_COMB,       // combine tiles
+  FP_COUNT
+};
+
+// Queue state at the start of the workspace: zero before the first call, and
+// left zero by every call that completes (the last workgroup to leave resets
+// it).  err is sticky: a wait that gave up (spin limit) sets it, and the
+// outputs of that call are undefined.
+struct FusedHdr {
+  unsigned next;    // next task to hand out
+  unsigned exited;  // workgroups that have left the queue
+  unsigned err;
+  unsigned pad;
+  unsigned done[FP_COUNT];  // finished tasks per phase
+};
+constexpr size_t kFusedHdrBytes = 256;
+
+struct FusedArgs {
+  FusedHdr* hdr;
+  unsigned start[FP_COUNT + 1];  // task ranges of the phases, in queue order
+  // routing
+  const uint16_t* x;
+  const int32_t* token_ids;
+  const uint16_t* w_router;
+  const float* bias;
+  int64_t T;
+  int D, E, k, mode;
+  int route_var;  // 0: small-T logit tiles 1x1x16, 1: 4x2x4, 2: LDS tiles 16x4, 3: hash
+  int route_gy;   // expert tiles of the logit tiling
+  int topk_c;     // keys per lane of the top-k (1, 2, 4, 8, 16)
+  float* logits;
+  int32_t* idx;
+  float* tw;
+  uint64_t* mask;
+  int64_t W;       // mask words per expert
+  int64_t n_zero;  // mask words the logit tasks clear
+  // permutation
+  int32_t* wprefix;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* row_token;
+  int32_t* pair_row;
+  TileJobs jobs;  // routed gate/up and down tile tables
+  int n_perm;
+  // expert GEMMs
+  GemmSeg gu_r, gu_s, dn_r, dn_s;
+  const int4* tab_gu;
+  const int4* tab_dn;
+  // Finished gate/up tiles per routed row tile, indexed by the tile's first
+  // row (row tiles of different experts never share a first row): a down
+  // tile starts once all gu_ntiles feature tiles of its rows are done.
+  // Cleared by the permutation tasks.  [R]
+  unsigned* row_done;
+  int gu_ntiles;
+  int sh_mt;  // row tiles of the shared expert
+  int glu;
+  // combine
+  const uint16_t* o;
+  const uint16_t* s;  // shared expert rows or nullptr
+  int comb_tpt, comb_gy;
+  uint16_t* y;
+};
+
+// Tile configuration of the fused kernel by rows per expert (bit-identical
+// choices): 0 <= 2, 1 <= 16, 2 <= 96, 3 above.
+int fused_cfg(int64_t rows_per_group_hint, bool fp4);
+// Row tile and feature tiles of a fused configuration.
+void fused_tiles(int cfg, int* BM, int* BN_gu, int* BN_dn);
+// Workgroups that one launch may use: resident capacity of the kernel (at
+// most ntasks).  Returns 0 on a HIP error.
+int64_t fused_grid(int cfg, bool fp4, int64_t ntasks);
+hipError_t launch_layer_fused(const FusedArgs& a, int cfg, bool fp4, int64_t grid,
+                              hipStream_t s);
+
 hipError_t launch_combine(const void* expert_out, const int32_t* topk_idx, const float* topk_w,
                           const int32_t* pair_row, const void* shared_out, int64_t T, int k,
                           int D, int act, void* y, hipStream_t s);

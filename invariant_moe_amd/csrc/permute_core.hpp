@@ -13,34 +13,36 @@ namespace moe {
 // this many words (E * ceil(T / 64)); otherwise prefixes go through wprefix.
 constexpr int kPermLdsWords = 4096;
 
-template <int NT>
+// LDSW: mask words that may be kept in LDS (0: never); OMAP: entries of the
+// row-tile owner map (more row tiles fall back to a binary search).
+template <int NT, int LDSW = kPermLdsWords, int OMAP = kTileOwnerMax>
 struct PermuteLds {
   int soff[MOE_MAX_EXPERTS + 1];
   int mpre[MOE_MAX_EXPERTS + 1];
   int wsum[2 * (NT / 64)];
-  int omap[kTileOwnerMax];
-  unsigned long long wmask[kPermLdsWords];
-  int wpre[kPermLdsWords];
+  int omap[OMAP];
+  unsigned long long wmask[LDSW > 0 ? LDSW : 1];
+  int wpre[LDSW > 0 ? LDSW : 1];
 };
 
 // counts, offsets, per-(expert, word) prefixes, the tile tables of the
 // grouped GEMMs that follow, then the scatter.  Run by nwg workgroups of NT
 // threads: each computes the counts and prefixes itself (all get the same
 // values), then writes its share of the tables and of the scatter.
-template <int NT>
+template <int NT, int LDSW, int OMAP, bool CO = false>
 __device__ void permute_core(const int32_t* __restrict__ topk_idx, int64_t T, int k, int E,
                              const uint64_t* __restrict__ mask, int64_t W,
                              int32_t* __restrict__ wprefix, int32_t* __restrict__ counts,
                              int32_t* __restrict__ offsets, int32_t* __restrict__ row_token,
                              int32_t* __restrict__ pair_row, const TileJobs& jobs,
-                             PermuteLds<NT>& L, int wg, int nwg) {
+                             PermuteLds<NT, LDSW, OMAP>& L, int wg, int nwg) {
   const int BM = jobs.n > 0 ? jobs.BM : 1;
   const int tid = threadIdx.x;
   const int Wi = (int)W;
   // LDS path for small masks of several words per expert (measured: 0.5 us
   // faster at 512 tokens x 64 experts, slower with a single word, and the
   // one-thread-per-expert walk is faster for masks past the LDS limit).
-  const bool in_lds = W >= 2 && (int64_t)E * W <= kPermLdsWords;
+  const bool in_lds = LDSW > 0 && W >= 2 && (int64_t)E * W <= LDSW && E <= NT;
 
   // The scatter's first four pairs per thread do not depend on anything
   // below: their expert ids are loaded first.  Indices fit in 32 bits
@@ -90,7 +92,7 @@ __device__ void permute_core(const int32_t* __restrict__ topk_idx, int64_t T, in
         pre += __popcll(L.wmask[e1 * Wi + b]);
       }
       if (s1 == tpe - 1) {
-        if (wg == 0) counts[e1] = incl;
+        if (wg == 0) Out<CO>::put(&counts[e1], incl);
         L.soff[e1] = incl;
         L.mpre[e1] = (incl + BM - 1) / BM;
       }
@@ -112,7 +114,7 @@ __device__ void permute_core(const int32_t* __restrict__ topk_idx, int64_t T, in
           c += __popcll(v[u]);
         }
       }
-      if (wg == 0) counts[e] = c;
+      if (wg == 0) Out<CO>::put(&counts[e], c);
       L.soff[e] = c;
       L.mpre[e] = (c + BM - 1) / BM;
     }
@@ -120,10 +122,10 @@ __device__ void permute_core(const int32_t* __restrict__ topk_idx, int64_t T, in
   __syncthreads();
   tile_scan2<NT>(L.soff, L.mpre, E, L.wsum);
   if (wg == 0)
-    for (int e = tid; e <= E; e += NT) offsets[e] = L.soff[e];
+    for (int e = tid; e <= E; e += NT) Out<CO>::put(&offsets[e], L.soff[e]);
   if (jobs.n > 0) {
-    const bool map = build_tile_owner<NT>(L.mpre, E, L.omap);
-    build_tile_tables<NT>(jobs, L.soff, L.mpre, map ? L.omap : nullptr, E, wg, nwg);
+    const bool map = build_tile_owner<NT, OMAP>(L.mpre, E, L.omap);
+    build_tile_tables<NT, CO>(jobs, L.soff, L.mpre, map ? L.omap : nullptr, E, wg, nwg);
   }
   // The LDS words and prefixes, or the wprefix entries this workgroup wrote,
   // are visible after the barriers above.  Four pairs per thread per round.
@@ -154,14 +156,14 @@ __device__ void permute_core(const int32_t* __restrict__ topk_idx, int64_t T, in
       const unsigned p = p0 + u * NT;
       if (p >= R) continue;
       if (e[u] < 0 || e[u] >= E) {  // outside the contract; keep memory safe
-        pair_row[p] = -1;
+        Out<CO>::put(&pair_row[p], -1);
         continue;
       }
       const unsigned t = p / uk;
       const uint64_t below = word[u] & ((1ull << (t & 63)) - 1ull);
       const int32_t r = L.soff[e[u]] + pre_b[u] + __popcll(below);
-      row_token[r] = (int32_t)t;
-      pair_row[p] = r;
+      Out<CO>::put(&row_token[r], (int32_t)t);
+      Out<CO>::put(&pair_row[p], r);
     }
   }
 }

@@ -99,7 +99,7 @@ __device__ __forceinline__ void topk_load(const float* __restrict__ row, int E, 
   }
 }
 
-template <int C>
+template <int C, bool CO = false>
 __device__ __forceinline__ bool topk_select(const float (&raw)[C], const float (&bias_v)[C],
                                             bool has_bias, int E, int k, int mode,
                                             int32_t* __restrict__ idx, float* __restrict__ w,
@@ -165,8 +165,8 @@ __device__ __forceinline__ bool topk_select(const float (&raw)[C], const float (
     Z = Z + readlane_f32(z, src);
   }
   if (act) {
-    idx[lane] = my_id;
-    w[lane] = z / Z;
+    Out<CO>::put(&idx[lane], my_id);
+    Out<CO>::put(&w[lane], z / Z);
   }
   my_id_out = my_id;
   return act;
@@ -183,7 +183,7 @@ __device__ __forceinline__ void topk_load_bias(const float* __restrict__ bias, i
   }
 }
 
-template <int C>
+template <int C, bool CO = false>
 __device__ __forceinline__ bool topk_token(const float* __restrict__ logit_row,
                                            const float* __restrict__ bias, int E, int k,
                                            int mode, int32_t* __restrict__ idx,
@@ -191,7 +191,7 @@ __device__ __forceinline__ bool topk_token(const float* __restrict__ logit_row,
   float raw[C], bias_v[C];
   topk_load<C>(logit_row, E, raw);
   topk_load_bias<C>(bias, E, bias_v);
-  return topk_select<C>(raw, bias_v, bias != nullptr, E, k, mode, idx, w, my_id_out);
+  return topk_select<C, CO>(raw, bias_v, bias != nullptr, E, k, mode, idx, w, my_id_out);
 }
 
 }  // namespace moe

@@ -22,15 +22,23 @@ __device__ __forceinline__ int tile_group_rows(const int* soff, int e, int64_t M
   return (a < 0 || (int64_t)b > M || b < a) ? 0 : b - a;
 }
 
-// Exclusive scans of a[0..n) and b[0..n) (n <= NT) in place, sharing the
-// barriers; the totals go to a[n] and b[n].  Lanes scan within their wave,
-// then the first wave scans the NT/64 wave sums.  wsum: 2 * (NT/64) ints.
+// Exclusive scans of a[0..n) and b[0..n) in place, sharing the barriers; the
+// totals go to a[n] and b[n].  Thread i takes the run of c = ceil(n / NT)
+// consecutive entries from i*c (one entry when n <= NT); lanes scan the run
+// sums within their wave, then the first wave scans the NT/64 wave sums.
+// wsum: 2 * (NT/64) ints.
 template <int NT>
 __device__ void tile_scan2(int* a, int* b, int n, int* wsum) {
   static_assert(NT / 64 <= 64, "one wave scans the wave sums");
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int xa = tid < n ? a[tid] : 0, xb = tid < n ? b[tid] : 0;
+  const int c = (n + NT - 1) / NT;
+  const int i0 = min(tid * c, n), i1 = min(i0 + c, n);
+  int xa = 0, xb = 0;
+  for (int i = i0; i < i1; ++i) {
+    xa += a[i];
+    xb += b[i];
+  }
   int ia = xa, ib = xb;
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) {
@@ -66,9 +74,13 @@ __device__ void tile_scan2(int* a, int* b, int n, int* wsum) {
     }
   }
   __syncthreads();
-  if (tid < n) {
-    a[tid] = wsum[wave] + ia - xa;
-    b[tid] = wsum[NW + wave] + ib - xb;
+  int pa = wsum[wave] + ia - xa, pb = wsum[NW + wave] + ib - xb;
+  for (int i = i0; i < i1; ++i) {
+    const int va = a[i], vb = b[i];
+    a[i] = pa;
+    b[i] = pb;
+    pa += va;
+    pb += vb;
   }
   __syncthreads();
 }
@@ -79,10 +91,10 @@ constexpr int kTileOwnerMax = 8192;
 
 // Builds omap from the exclusive m-tile prefix mpre[E+1] (call after the
 // scan, by all threads; ends with a barrier).  Returns false (map unused)
-// when there are more than kTileOwnerMax row tiles.
-template <int NT>
+// when there are more than OMAP row tiles.
+template <int NT, int OMAP = kTileOwnerMax>
 __device__ bool build_tile_owner(const int* mpre, int E, int* omap) {
-  const bool fits = mpre[E] <= kTileOwnerMax;
+  const bool fits = mpre[E] <= OMAP;
   if (fits)
     for (int e = threadIdx.x; e < E; e += NT)
       for (int m = mpre[e]; m < mpre[e + 1]; ++m) omap[m] = e;
@@ -98,7 +110,7 @@ __device__ bool build_tile_owner(const int* mpre, int E, int* omap) {
 // tile range holds floor(li / nt).  All jobs share jobs.BM (the host planner
 // guarantees it); all counts fit in int32 (it rejects launches of 2^31 or
 // more workgroups).
-template <int NT>
+template <int NT, bool CO = false>
 __device__ void build_tile_tables(const TileJobs& jobs, const int* soff, const int* mpre,
                                   const int* omap, int E, int wg, int nwg) {
   const int BM = jobs.BM;
@@ -149,7 +161,7 @@ __device__ void build_tile_tables(const TileJobs& jobs, const int* soff, const i
                         (int)ntile * BN);
         }
       }
-      J.table[b] = d;
+      Out<CO>::put4(&J.table[b], d);
     }
   }
 }

@@ -61,3 +61,22 @@ def mxfp4_decode_bf16(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
 def mxfp4_pack(codes: np.ndarray) -> np.ndarray:
     """E2M1 codes [..., cols] -> bytes [..., cols/2], element 2i in the low nibble."""
     return (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+
+
+_layers = {}
+
+
+def device_layer(cid):
+    """(DeviceLayer, MoELayer) of a recipe, uploaded once; one large layer is
+    kept resident at a time (recipe 4 shares recipe 3's weights)."""
+    import synth
+    from synth import device as sdev
+    if cid == 4:  # the decode recipe runs the prefill recipe's layer
+        cid = 3
+    if cid not in _layers:
+        _layers.clear()
+        cfg = synth.CONFIGS[cid]
+        dl = sdev.upload_layer(cfg, "cuda",
+                               progress=lambda e, n: banner(f"recipe {cid}: {e}/{n} experts"))
+        _layers[cid] = (dl, sdev.layer_object(dl))
+    return _layers[cid]

@@ -13,7 +13,7 @@ import torch
 import invariant_moe_amd as moe
 import oracle
 import synth
-from gpu_util import banner, dev, rel_l2, requires_gpu, to_np, tol_for
+from gpu_util import banner, dev, device_layer, rel_l2, requires_gpu, to_np, tol_for
 from gpu_util import mxfp4_decode_bf16 as _decode_bf16, mxfp4_pack as _pack
 from synth import device as sdev
 
@@ -29,17 +29,8 @@ def _oracle_layer(cfg, x, ids, experts=None):
                                 cfg.wdtype)
 
 
-_layers = {}
-
-
 def _device_layer(cid):
-    if cid not in _layers:
-        cfg = synth.CONFIGS[cid]
-        _layers.clear()  # keep one large layer resident at a time
-        dl = sdev.upload_layer(cfg, "cuda",
-                               progress=lambda e, n: banner(f"recipe {cid}: {e}/{n} experts"))
-        _layers[cid] = (dl, sdev.layer_object(dl))
-    return _layers[cid]
+    return device_layer(cid)
 
 
 @pytest.mark.parametrize("cid", [1, 2])
@@ -405,7 +396,7 @@ def test_decode_sweep_bitwise_and_oracle():
     bitwise equal to the same token's row at T = 64; a sample vs the oracle."""
     cfg = synth.CONFIGS[4]
     banner("decode sweep recipe 4")
-    dl, layer = _device_layer(4) if 3 not in _layers else _layers[3]
+    dl, layer = _device_layer(4)
     pool = synth.x_tokens(cfg)  # 64 tokens
     y64 = to_np(layer.forward(dev(pool)))
     for T in range(1, 65):
