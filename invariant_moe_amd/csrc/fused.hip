@@ -34,15 +34,21 @@ namespace moe {
 // Tile shapes of the fused configurations (256-thread workgroups).
 template <int CFG>
 struct FusedTiles;
+// The decode shapes use wide feature tiles.  The kernel runs one workgroup
+// per CU, and a timeline of its tasks (per-task timestamps, T = 1..64) showed
+// each workgroup's weight stream bound by the latency of its K-stage loop, not
+// by the loads in flight (more stages in flight changed nothing): a 16 x 64
+// down tile streamed about 11 GB/s per workgroup.  Wider tiles move more bytes
+// per loop step.
 template <>
 struct FusedTiles<0> {  // <= 2 rows per expert (decode)
-  static constexpr int BM = 16, GBN = 64, GWM = 1, GWN = 4, GP = 4;
-  static constexpr int DBN = 64, DWM = 1, DWN = 4, DP = 4;
+  static constexpr int BM = 16, GBN = 128, GWM = 1, GWN = 4, GP = 4;
+  static constexpr int DBN = 256, DWM = 1, DWN = 4, DP = 4;
 };
 template <>
 struct FusedTiles<1> {  // <= 16 rows per expert
-  static constexpr int BM = 32, GBN = 64, GWM = 1, GWN = 4, GP = 4;
-  static constexpr int DBN = 64, DWM = 1, DWN = 4, DP = 4;
+  static constexpr int BM = 32, GBN = 128, GWM = 1, GWN = 4, GP = 4;
+  static constexpr int DBN = 128, DWM = 1, DWN = 4, DP = 4;
 };
 template <>
 struct FusedTiles<2> {  // <= 96 rows per expert (bf16 weights)
