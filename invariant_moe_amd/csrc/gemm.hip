@@ -428,7 +428,8 @@ GemmPlan plan_w4a8_gemm(const SegShape& seg, bool gated, int64_t rows_per_group_
   L.seg_mask = 1;
   // Measured at D=7168, I=2048: 64 x 64 is the fastest at 8 rows per expert
   // (most workgroups for the weight stream), 64 x 128 at 64 rows (half the
-  // token re-reads, -12 %), 128 x 128 at 256 rows.
+  // token re-reads, -12 %), 128 x 128 at 256 rows.  A 64 x 256 tile on 2 x 4
+  // waves at 64 rows lost 8 % to 64 x 128 (fewer workgroups per weight byte).
   L.cfg = rows_per_group_hint > 96   ? TILE_W4A8_128
           : rows_per_group_hint > 16 ? TILE_W4A8_N128
                                      : TILE_W4A8;
