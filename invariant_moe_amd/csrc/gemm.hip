@@ -373,7 +373,12 @@ static int pick_tile_cfg(bool gated, int64_t rows_per_group_hint, bool fp4) {
   if (fp4 && rows_per_group_hint <= 96) return gated ? TILE_128x64_2x2_P2 : TILE_128x128_2x2_P2;
   if (rows_per_group_hint <= 96) return gated ? TILE_64x32_4x1_P2 : TILE_64x64_4x1_P2;
   // many rows per expert: 128 x 128 tiles (gate/up on 8 waves, two per SIMD;
-  // the down GEMM measured 1.96 ms on 4 waves and 2.23 ms on 8 at recipe 3)
+  // the down GEMM measured 1.96 ms on 4 waves and 2.23 ms on 8 at recipe 3).
+  // Stages brought into LDS by direct loads (global_load_lds_dwordx4, no
+  // staging registers, a 3- or 4-stage LDS ring) measured no faster at
+  // recipe 3: gate/up 3.35 ms on the 128 x 128 tile with 3 stages, down
+  // 2.16 ms on 8 waves with 4; 64-row tiles with a 4-stage ring of mostly
+  // weights, 4.22 and 2.20 ms.
   return gated ? TILE_128x128_2x4_P2 : TILE_128x128_2x2_P2;
 }
 
