@@ -94,7 +94,7 @@ class Hip:
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("gemm.hip", "common.hpp", "kernels.hpp"):
+    for f in ("gemm.hip", "gemm_core.hpp", "tiles.hpp", "common.hpp", "kernels.hpp"):
         with open(os.path.join(ROOT, "invariant_moe_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

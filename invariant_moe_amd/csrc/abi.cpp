@@ -71,7 +71,11 @@ struct Carver {
 
 // The two grouped GEMMs of the expert FFN (gate/up, then down) as the host
 // planner sees them: routed experts grouped by the device offsets, plus the
-// shared expert as one group of T rows.
+// shared expert as one group of T rows.  (Measured on MI355X: the shared
+// expert in launches of its own on a second stream, concurrent with routing
+// and permutation, was slower at prefill, 5.87 against 5.83 ms per layer at
+// T=4096, and at decode, 156 against 153 us at T=1: it slowed the small
+// kernels it overlapped and added a cross-queue wait.)
 struct FfnPlans {
   moe::GemmPlan up, dn;
 };
