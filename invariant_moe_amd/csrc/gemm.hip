@@ -369,7 +369,8 @@ static int pick_tile_cfg(bool gated, int64_t rows_per_group_hint, bool fp4) {
   if (rows_per_group_hint <= 16) return TILE_32x64_1x4_P4;
   // MXFP4 weights: 128-row tiles (measured at 64 rows per expert: 1.99 ms for
   // the recipe-5 gate/up launch, against 2.69 ms with 64 x 128 tiles on 1 x 4
-  // waves, whose waves each decode and read all 64 token rows)
+  // waves, whose waves each decode and read all 64 token rows, and 2.45 ms
+  // with 64 x 64 tiles on 2 x 2 waves, where no wave idles)
   if (fp4 && rows_per_group_hint <= 96) return gated ? TILE_128x64_2x2_P2 : TILE_128x128_2x2_P2;
   if (rows_per_group_hint <= 96) return gated ? TILE_64x32_4x1_P2 : TILE_64x64_4x1_P2;
   // many rows per expert: 128 x 128 tiles (gate/up on 8 waves, two per SIMD;
