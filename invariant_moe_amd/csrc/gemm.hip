@@ -364,7 +364,10 @@ static hipError_t launch_tile_cfg(int cfg, const GemmArgs& a, bool gated, int64_
 static int pick_tile_cfg(bool gated, int64_t rows_per_group_hint, bool fp4) {
   // At most two rows per expert (decode): the gate/up launch in single-wave
   // workgroups spreads the weight stream evenly over the CUs (measured 3-4 %
-  // faster than two-wave 16 x 32 tiles from T=1 to T=4).
+  // faster than two-wave 16 x 32 tiles from T=1 to T=4).  Down tiles of
+  // 16 x 16 and 16 x 32 measured the same as 16 x 64 at T=1; single-wave tiles
+  // that load both MFMA operands straight into registers (16-byte pieces of
+  // 16 rows per instruction, no LDS) streamed 30 % slower.
   if (rows_per_group_hint <= 2) return gated ? TILE_16x16_1x1_P4 : TILE_16x64_1x4_P4;
   if (rows_per_group_hint <= 16) return TILE_32x64_1x4_P4;
   // MXFP4 weights: 128-row tiles (measured at 64 rows per expert: 1.99 ms for
