@@ -48,6 +48,10 @@ constexpr int KT = 64;         // K per LDS stage (two MFMA k-steps)
 // MI355X, decode steps 9-10 % faster (gate/up weights at 6.0 instead of
 // 5.4 TB/s); in 128-row prefill tiles, where several m-tiles of an expert
 // re-read the panel from L2, it is 6 % slower, so those keep plain loads.
+// MXFP4 tiles keep them too: a stage reads only 32 bytes of a weight row, and
+// non-temporal loads then fetch each piece of a 128-byte line from HBM on its
+// own (measured 45 % slower at 64 rows per expert; the same for the FP4 x FP8
+// kernel, whose stages read 64 bytes of a row).
 __device__ __forceinline__ uint4 nt_load16(const uint8_t* p) {
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
