@@ -111,8 +111,9 @@ int64_t layer_table_entries(int64_t T, int D, int E, int k, int I, int Is, moe_d
 }
 
 // Plans of the layer's FFN when the routed experts run FP4 x FP8: the routed
-// GEMMs on the W4A8 kernel (64-row tiles), the bf16 shared expert on the bf16
-// kernel with 64-row tiles too, so one permutation launch writes all four
+// GEMMs on the W4A8 kernel, the bf16 shared expert on the bf16 kernel with
+// the tiles the planner picks for its T rows (its tables are dense, so they
+// need not share the routed row tile); one permutation launch writes all four
 // tile tables.
 struct W4a8Plans {
   moe::GemmPlan up_r, up_s, dn_r, dn_s;
@@ -125,11 +126,10 @@ W4a8Plans w4a8_plans(int64_t R, int64_t T, int D, int E, int I, int Is) {
   p.up_r = moe::plan_w4a8_gemm({true, R, E, D, I, 2}, true, hint);
   p.dn_r = moe::plan_w4a8_gemm({true, R, E, I, D, 2}, false, hint);
   p.shared = Is > 0;
-  if (p.shared) {  // the bf16 planner's tile for the same hint has the same row tile
+  if (p.shared) {
     const moe::SegShape su{false, T, 1, D, Is, 0}, sd{false, T, 1, Is, D, 0};
-    const int64_t sh = p.up_r.l[0].BM == 128 ? 128 : 64;
-    p.up_s = moe::plan_grouped_gemm(&su, 1, true, MOE_BF16, sh);
-    p.dn_s = moe::plan_grouped_gemm(&sd, 1, false, MOE_BF16, sh);
+    p.up_s = moe::plan_grouped_gemm(&su, 1, true, MOE_BF16, T);
+    p.dn_s = moe::plan_grouped_gemm(&sd, 1, false, MOE_BF16, T);
   }
   return p;
 }

@@ -460,8 +460,14 @@ int64_t plan_table_entries(const GemmPlan& p) {
 bool plan_tile_jobs(const GemmPlan& p, int4* tables, TileJobs& jobs) {
   for (int i = 0; i < p.n; ++i) {
     const PlanLaunch& L = p.l[i];
-    if (jobs.n == MOE_MAX_TILE_JOBS || (jobs.n > 0 && jobs.BM != L.BM)) return false;
-    jobs.BM = L.BM;
+    bool grouped = false;
+    for (int sg = 0; sg < p.nseg; ++sg)
+      if ((L.seg_mask & (1 << sg)) && p.seg[sg].grouped) grouped = true;
+    if (jobs.n == MOE_MAX_TILE_JOBS) return false;
+    if (grouped) {  // grouped segments of one call share their m-tile counts
+      if (jobs.BM > 0 && jobs.BM != L.BM) return false;
+      jobs.BM = L.BM;
+    }
     TileJob& J = jobs.job[jobs.n++];
     J = TileJob{};
     J.table = tables;
@@ -546,7 +552,7 @@ __global__ __launch_bounds__(1024) void k_tile_tables(const int32_t* __restrict_
     for (int sg = 0; sg < jobs.job[j].nseg; ++sg)
       if (jobs.job[j].grouped[sg]) M = jobs.job[j].M[sg];
   for (int e = threadIdx.x; e < E; e += 1024) {
-    mpre[e] = (tile_group_rows(soff, e, M) + jobs.BM - 1) / jobs.BM;
+    mpre[e] = jobs.BM > 0 ? (tile_group_rows(soff, e, M) + jobs.BM - 1) / jobs.BM : 0;
     unused[e] = 0;
   }
   __syncthreads();

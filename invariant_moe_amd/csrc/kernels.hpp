@@ -84,7 +84,9 @@ constexpr int MOE_MAX_TILE_JOBS = 4;
 struct TileJobs {
   TileJob job[MOE_MAX_TILE_JOBS];
   int n;
-  int BM;  // row tile shared by every job
+  int BM;  // row tile of the grouped segments, shared by every job that has
+           // one; a job of ungrouped segments only tiles by its own BM (0: no
+           // grouped job)
 };
 
 // zero / n_zero (optional): 64-bit words cleared for a later kernel of the call.

@@ -36,7 +36,7 @@ __device__ void permute_core(const int32_t* __restrict__ topk_idx, int64_t T, in
                              int32_t* __restrict__ offsets, int32_t* __restrict__ row_token,
                              int32_t* __restrict__ pair_row, const TileJobs& jobs,
                              PermuteLds<NT, LDSW, OMAP>& L, int wg, int nwg) {
-  const int BM = jobs.n > 0 ? jobs.BM : 1;
+  const int BM = jobs.BM > 0 ? jobs.BM : 1;  // no grouped job: the m-tile counts go unused
   const int tid = threadIdx.x;
   const int Wi = (int)W;
   // LDS path for small masks of several words per expert (measured: 0.5 us

@@ -107,9 +107,10 @@ __device__ bool build_tile_owner(const int* mpre, int E, int* omap) {
 // [E+1]; mpre: exclusive prefix [E+1] of ceil(rows_e / jobs.BM); omap: owner
 // map or nullptr.  Tiles of a grouped segment are numbered group-major, then
 // by feature tile, then by row tile, so tile li lies in the group whose row
-// tile range holds floor(li / nt).  All jobs share jobs.BM (the host planner
-// guarantees it); all counts fit in int32 (it rejects launches of 2^31 or
-// more workgroups).
+// tile range holds floor(li / nt).  Grouped segments are tiled by jobs.BM
+// (every job that has one shares it: the host planner guarantees it);
+// ungrouped ones by their job's BM.  All counts fit in int32 (the planner
+// rejects launches of 2^31 or more workgroups).
 template <int NT, bool CO = false>
 __device__ void build_tile_tables(const TileJobs& jobs, const int* soff, const int* mpre,
                                   const int* omap, int E, int wg, int nwg) {
@@ -117,13 +118,13 @@ __device__ void build_tile_tables(const TileJobs& jobs, const int* soff, const i
 #pragma unroll 1
   for (int j = 0; j < jobs.n; ++j) {  // uniform: job fields come from scalar loads
     const TileJob& J = jobs.job[j];
-    const int grid = (int)J.grid, BN = J.BN, nseg = J.nseg;
+    const int grid = (int)J.grid, BN = J.BN, nseg = J.nseg, DBM = J.BM;
     int tot[2] = {0, 0}, nt[2] = {1, 1}, Ms[2] = {0, 0}, grouped[2] = {0, 0};
     for (int sg = 0; sg < nseg; ++sg) {
       nt[sg] = (J.N[sg] + BN - 1) / BN;
       grouped[sg] = J.grouped[sg];
       Ms[sg] = (int)J.M[sg];
-      tot[sg] = grouped[sg] ? mpre[E] * nt[sg] : (Ms[sg] + BM - 1) / BM * nt[sg];
+      tot[sg] = grouped[sg] ? mpre[E] * nt[sg] : (Ms[sg] + DBM - 1) / DBM * nt[sg];
     }
     const int total = tot[0] + tot[1];
     const unsigned chunk = (unsigned)(total + 7) / 8u;
@@ -155,9 +156,9 @@ __device__ void build_tile_tables(const TileJobs& jobs, const int* soff, const i
           d = make_int4(soff[e] + (int)mtile * BM, min(BM, rows - (int)mtile * BM),
                         (sg << 16) | e, (int)ntile * BN);
         } else {
-          const unsigned mt = (unsigned)(Ms[sg] + BM - 1) / (unsigned)BM;
+          const unsigned mt = (unsigned)(Ms[sg] + DBM - 1) / (unsigned)DBM;
           const unsigned ntile = (unsigned)li / mt, mtile = (unsigned)li - ntile * mt;
-          d = make_int4((int)mtile * BM, min(BM, Ms[sg] - (int)mtile * BM), sg << 16,
+          d = make_int4((int)mtile * DBM, min(DBM, Ms[sg] - (int)mtile * DBM), sg << 16,
                         (int)ntile * BN);
         }
       }
