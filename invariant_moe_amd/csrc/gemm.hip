@@ -165,19 +165,27 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_grouped_gemm_w4a8(GemmAr
 
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // native: plain loads and stores
   u32x4 xr[XPT], wr[WPT];
-  uint32_t sc[SPT];
+  // Scale words of four consecutive stages (stage kt's word in slot kt % 4),
+  // loaded together every fourth stage: a row's scales span K / 32 bytes,
+  // and reading one 4-byte word of a line per stage let the line leave L2
+  // between stages.
+  uint32_t sc[SPT][4];
+  auto sload = [&](int kt) {  // kt % 4 == 0; words past the last stage are not loaded
+#pragma unroll
+    for (int i = 0; i < SPT; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (kt + j < nst) sc[i][j] = *reinterpret_cast<const uint32_t*>(scsrc[i] + (kt + j) * 4);
+  };
   // stage loads into registers, then into LDS (the arrays are passed, not
   // captured, so that they stay in registers)
-  auto gload = [&](u32x4 (&xq)[XPT], u32x4 (&wq)[WPT], uint32_t (&scq)[SPT], int kt) {
+  auto gload = [&](u32x4 (&xq)[XPT], u32x4 (&wq)[WPT], int kt) {
 #pragma unroll
     for (int i = 0; i < XPT; ++i) xq[i] = *reinterpret_cast<const u32x4*>(xsrc[i] + kt * KQ);
 #pragma unroll
     for (int i = 0; i < WPT; ++i) wq[i] = *reinterpret_cast<const u32x4*>(wsrc[i] + kt * (KQ / 2));
-#pragma unroll
-    for (int i = 0; i < SPT; ++i) scq[i] = *reinterpret_cast<const uint32_t*>(scsrc[i] + kt * 4);
   };
-  auto lstore = [&](const u32x4 (&xq)[XPT], const u32x4 (&wq)[WPT], const uint32_t (&scq)[SPT],
-                    int buf) {
+  auto lstore = [&](const u32x4 (&xq)[XPT], const u32x4 (&wq)[WPT], int slot, int buf) {
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
       const int c = tid + i * NT;
@@ -197,9 +205,9 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_grouped_gemm_w4a8(GemmAr
     for (int i = 0; i < SPT; ++i) {
       const int w = tid + i * NT;
       if (w < BM)
-        ssx[buf][w] = scq[i];
+        ssx[buf][w] = sc[i][slot];
       else if (w < SW)
-        ssw[buf][w - BM] = scq[i];
+        ssw[buf][w - BM] = sc[i][slot];
     }
   };
   const int g4 = lane >> 4, r16 = lane & 15;
@@ -232,15 +240,26 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_grouped_gemm_w4a8(GemmAr
       }
   };
 
-  gload(xr, wr, sc, 0);
-  lstore(xr, wr, sc, 0);
+  sload(0);
+  gload(xr, wr, 0);
+  lstore(xr, wr, 0, 0);
   __syncthreads();
-  for (int kt = 0; kt < nst; ++kt) {
-    const bool more = kt + 1 < nst;  // uniform
-    if (more) gload(xr, wr, sc, kt + 1);
-    compute(kt & 1);
-    if (more) lstore(xr, wr, sc, (kt + 1) & 1);
-    __syncthreads();
+  // four stages per iteration, so that the scale slot of each is static
+  for (int k4 = 0; k4 < nst; k4 += 4) {
+    static_for<0, 4>([&](auto qc) {
+      constexpr int q = decltype(qc)::value;
+      const int kt = k4 + q;
+      if (kt < nst) {  // uniform
+        const bool more = kt + 1 < nst;
+        if (more) {
+          if (q == 3) sload(kt + 1);  // the next four stages' scale words
+          gload(xr, wr, kt + 1);
+        }
+        compute(kt & 1);
+        if (more) lstore(xr, wr, (q + 1) & 3, (kt + 1) & 1);
+        __syncthreads();
+      }
+    });
   }
 
   // epilogue (as the bf16 kernel): features n = base + 4*(lane/16) + v of token
