@@ -168,7 +168,9 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_grouped_gemm_w4a8(GemmAr
   // Scale words of four consecutive stages (stage kt's word in slot kt % 4),
   // loaded together every fourth stage: a row's scales span K / 32 bytes,
   // and reading one 4-byte word of a line per stage let the line leave L2
-  // between stages.
+  // between stages (measured at recipe 5: gate/up HBM reads 5.91 -> 5.41 GB,
+  // 1.34 -> 1.27 ms).  Loading the weight codes of two stages together (the
+  // two 64-byte halves of a row's line) read 5.13 GB but took 1.38 ms.
   uint32_t sc[SPT][4];
   auto sload = [&](int kt) {  // kt % 4 == 0; words past the last stage are not loaded
 #pragma unroll
