@@ -170,7 +170,8 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_grouped_gemm_w4a8(GemmAr
   // and reading one 4-byte word of a line per stage let the line leave L2
   // between stages (measured at recipe 5: gate/up HBM reads 5.91 -> 5.41 GB,
   // 1.34 -> 1.27 ms).  Loading the weight codes of two stages together (the
-  // two 64-byte halves of a row's line) read 5.13 GB but took 1.38 ms.
+  // two 64-byte halves of a row's line) read 5.13 GB but took 1.38 ms, and
+  // 6.13 GB and 1.62 ms with non-temporal loads.
   uint32_t sc[SPT][4];
   auto sload = [&](int kt) {  // kt % 4 == 0; words past the last stage are not loaded
 #pragma unroll
