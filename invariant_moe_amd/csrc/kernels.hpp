@@ -209,7 +209,7 @@ struct FusedArgs {
 };
 
 // Tile configuration of the fused kernel by rows per expert (bit-identical
-// choices): 0 <= 2, 1 <= 16, 2 <= 96, 3 above.
+// choices): 0 <= 2, 1 <= 16, 2 above (either weight format).
 int fused_cfg(int64_t rows_per_group_hint, bool fp4);
 // Row tile and feature tiles of a fused configuration.
 void fused_tiles(int cfg, int* BM, int* BN_gu, int* BN_dn);
