@@ -607,6 +607,21 @@ def main():
     kern_ms = np.array([[hip.elapsed_ms(kev[i][6], kev[i][7]),
                          hip.elapsed_ms(kev[i][8], kev[i][9])] for i in range(K2)]).mean(0)
     gu_ms = float(kern_ms[0])
+    # Cold against warm last-level cache (the 256 MB MALL): the passes above
+    # rotate nrep weight copies so that no step finds its weights cached; one
+    # copy repeated lets a layer whose weights fit in the cache run warm.
+    # With one copy the weights are far past the cache and every step is cold.
+    mall = {"cache_bytes": 256 << 20, "routed_weight_bytes": int(wbytes_routed),
+            "weight_copies": nrep, "cold_ms_per_step": round(ms_per_step, 5),
+            "warm_ms_per_step": None}
+    if nrep > 1:
+        torch.cuda.synchronize()
+        hip.record(ev0, sptr)
+        for i in range(K):
+            layers[0].forward(x, ids, out=y)
+        hip.record(ev1, sptr)
+        torch.cuda.synchronize()
+        mall["warm_ms_per_step"] = round(hip.elapsed_ms(ev0, ev1) / K, 5)
     print("[bench] layer timed", file=sys.stderr, flush=True)
 
     tail = w4a8 = decode = fused = None
@@ -722,6 +737,7 @@ def main():
                     "p50": round(float(np.percentile(step_ms, 50)), 5),
                     "p90": round(float(np.percentile(step_ms, 90)), 5)},
         "clocks": clocks.summary(),
+        "mall": mall,
         "tail": tail,
         "w4a8": w4a8,
         "decode": decode,
