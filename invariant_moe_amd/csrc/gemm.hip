@@ -319,9 +319,8 @@ enum TileCfg {
   TILE_32x64_1x4_P4,
   TILE_64x32_4x1_P2,      // tens of rows per expert
   TILE_64x64_4x1_P2,
-  TILE_128x64_2x2_P2,     // MXFP4 weights with tens of rows per expert
-  TILE_128x128_2x2_P2,    // prefill
-  TILE_128x128_2x4_P2,    // prefill gate/up: 8 waves, two per SIMD
+  TILE_128x128_2x4_P2,    // gate/up above 96 rows per expert (MXFP4: above 16), 8 waves
+  TILE_128x256_2x4_P2,    // down, the same brackets, 8 waves
   TILE_COUNT,
   TILE_F32 = 100,         // fp32 VALU kernel, 16 x 16 tiles
   TILE_W4A8 = 200,        // FP4 x FP8 kernel, 64 x 64 tiles on 2 x 2 waves
@@ -340,9 +339,8 @@ static TileShape tile_shape(int cfg) {
     case TILE_32x64_1x4_P4: return {32, 64};
     case TILE_64x32_4x1_P2: return {64, 32};
     case TILE_64x64_4x1_P2: return {64, 64};
-    case TILE_128x64_2x2_P2: return {128, 64};
-    case TILE_128x128_2x2_P2: return {128, 128};
     case TILE_128x128_2x4_P2: return {128, 128};
+    case TILE_128x256_2x4_P2: return {128, 256};
     case TILE_W4A8: return {64, 64};
     case TILE_W4A8_N128: return {64, 128};
     case TILE_W4A8_128: return {128, 128};
@@ -352,9 +350,8 @@ static TileShape tile_shape(int cfg) {
 
 // The (configuration, branch, weight format) combinations the planner can
 // select: every configuration for either format, since a launch of one
-// format may carry the configuration chosen for the other (shared and routed
-// experts in different formats), except the 128 x 64 gate/up tile, which only
-// MXFP4 launches get (a bf16 launch takes its twin of the same row tile).
+// format carries the configuration chosen for the other when shared and
+// routed experts come in different formats.
 template <bool FP4>
 static hipError_t launch_tile_cfg(int cfg, const GemmArgs& a, bool gated, int64_t grid,
                                   hipStream_t st, LaunchEvents ev) {
@@ -363,9 +360,6 @@ static hipError_t launch_tile_cfg(int cfg, const GemmArgs& a, bool gated, int64_
       case TILE_16x16_1x1_P4: return launch_one<16, 16, 1, 1, 4, true, FP4>(a, grid, st, ev);
       case TILE_32x64_1x4_P4: return launch_one<32, 64, 1, 4, 4, true, FP4>(a, grid, st, ev);
       case TILE_64x32_4x1_P2: return launch_one<64, 32, 4, 1, 2, true, FP4>(a, grid, st, ev);
-      case TILE_128x64_2x2_P2:
-        if constexpr (FP4) return launch_one<128, 64, 2, 2, 2, true, true>(a, grid, st, ev);
-        break;
       case TILE_128x128_2x4_P2: return launch_one<128, 128, 2, 4, 2, true, FP4>(a, grid, st, ev);
       default: break;
     }
@@ -374,7 +368,7 @@ static hipError_t launch_tile_cfg(int cfg, const GemmArgs& a, bool gated, int64_
       case TILE_16x64_1x4_P4: return launch_one<16, 64, 1, 4, 4, false, FP4>(a, grid, st, ev);
       case TILE_32x64_1x4_P4: return launch_one<32, 64, 1, 4, 4, false, FP4>(a, grid, st, ev);
       case TILE_64x64_4x1_P2: return launch_one<64, 64, 4, 1, 2, false, FP4>(a, grid, st, ev);
-      case TILE_128x128_2x2_P2: return launch_one<128, 128, 2, 2, 2, false, FP4>(a, grid, st, ev);
+      case TILE_128x256_2x4_P2: return launch_one<128, 256, 2, 4, 2, false, FP4>(a, grid, st, ev);
       default: break;
     }
   }
@@ -392,29 +386,25 @@ static int pick_tile_cfg(bool gated, int64_t rows_per_group_hint, bool fp4) {
   // 16 rows per instruction, no LDS) streamed 30 % slower.
   if (rows_per_group_hint <= 2) return gated ? TILE_16x16_1x1_P4 : TILE_16x64_1x4_P4;
   if (rows_per_group_hint <= 16) return TILE_32x64_1x4_P4;
-  // MXFP4 weights: 128-row tiles (measured at 64 rows per expert: 1.99 ms for
-  // the recipe-5 gate/up launch, against 2.69 ms with 64 x 128 tiles on 1 x 4
-  // waves, whose waves each decode and read all 64 token rows, and 2.45 ms
-  // with 64 x 64 tiles on 2 x 2 waves, where no wave idles)
-  if (fp4 && rows_per_group_hint <= 96) return gated ? TILE_128x64_2x2_P2 : TILE_128x128_2x2_P2;
+  // MXFP4 weights: 128-row tiles on 8 waves, those of the empty row block
+  // loading and staging for the others.  Measured at 64 rows per expert
+  // (recipe-5 gate/up, down): 1.97 and 1.00 ms; 128 x 64 gate/up and
+  // 128 x 128 down on 2 x 2 waves 1.99 and 1.05 ms; 64 x 128 on 1 x 4 waves
+  // (each wave decodes and reads all 64 token rows) 2.69 ms; 64 x 64 on 2 x 2
+  // waves, where no wave idles, 2.45 ms.
+  if (fp4 && rows_per_group_hint <= 96) return gated ? TILE_128x128_2x4_P2 : TILE_128x256_2x4_P2;
   if (rows_per_group_hint <= 96) return gated ? TILE_64x32_4x1_P2 : TILE_64x64_4x1_P2;
-  // many rows per expert: 128 x 128 tiles (gate/up on 8 waves, two per SIMD;
-  // the down GEMM measured 1.96 ms on 4 waves and 2.23 ms on 8 at recipe 3).
+  // many rows per expert: gate/up 128 x 128 and down 128 x 256 tiles, both
+  // on 8 waves, two per SIMD (the down GEMM at recipe 3: 1.84 ms, against
+  // 1.94 ms for 128 x 128 on 4 waves and 2.23 ms for 128 x 128 on 8; 5.33
+  // against 5.64 ms at T=16384).
   // Stages brought into LDS by direct loads (global_load_lds_dwordx4, no
   // staging registers, a 3- or 4-stage LDS ring) measured no faster at
   // recipe 3: gate/up 3.35 ms on the 128 x 128 tile with 3 stages, down
   // 2.16 ms on 8 waves with 4; 64-row tiles with a 4-stage ring of mostly
   // weights, 4.22 and 2.20 ms; register-path 64 x 64 (gate/up) and 64 x 128
   // (down) tiles on 2 x 2 waves, three workgroups per CU, 4.48 and 2.27 ms.
-  return gated ? TILE_128x128_2x4_P2 : TILE_128x128_2x2_P2;
-}
-
-// Configuration of one launch whose weights are bf16 (fp4 == false) or MXFP4
-// within a layer planned as cfg: a bf16 launch next to MXFP4 routed experts
-// (the shared expert) takes the bf16 configuration with the same row tile.
-static int launch_cfg_for_format(int cfg, bool gated, bool fp4) {
-  if (!fp4 && gated && cfg == TILE_128x64_2x2_P2) return TILE_128x128_2x4_P2;
-  return cfg;
+  return gated ? TILE_128x128_2x4_P2 : TILE_128x256_2x4_P2;
 }
 
 GemmPlan plan_grouped_gemm(const SegShape* segs, int nseg, bool gated, int act,
@@ -434,8 +424,7 @@ GemmPlan plan_grouped_gemm(const SegShape* segs, int nseg, bool gated, int act,
   for (int l = 0; l < nl; ++l) {
     PlanLaunch& L = p.l[p.n];
     L.seg_mask = split ? (1 << l) : (nseg == 2 ? 3 : 1);
-    L.cfg = cfg == TILE_F32 ? cfg
-                            : launch_cfg_for_format(cfg, gated, segs[split ? l : 0].wfmt != 0);
+    L.cfg = cfg;  // every tile configuration is compiled for both weight formats
     const TileShape ls = tile_shape(L.cfg);
     L.BM = ls.BM;
     L.BN = ls.BN;
