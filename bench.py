@@ -22,6 +22,7 @@ import ctypes
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -92,11 +93,20 @@ class Hip:
         return ms.value
 
 
+def _code_only(text: str) -> str:
+    """C++ source without its comments, trailing blanks and empty lines."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(ln.rstrip() for ln in text.splitlines() if ln.strip())
+
+
 def kernel_source_hash() -> str:
+    """Hash of the code (comments left out) of the GEMM kernels and their
+    tile tables: a counter summary stays valid while this is unchanged."""
     h = hashlib.sha256()
     for f in ("gemm.hip", "gemm_core.hpp", "tiles.hpp", "common.hpp", "kernels.hpp"):
-        with open(os.path.join(ROOT, "invariant_moe_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "invariant_moe_amd", "csrc", f)) as fh:
+            h.update(f.encode() + b"\0" + _code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -117,9 +117,10 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_grouped_gemm_w4a8(GemmAr
   const int wm = wave / WN, wn = wave % WN;
   // In 128-row tiles a wave whose rows all lie past the tile's valid rows
   // issues no MFMA (it still loads and stages its share of each stage): an
-  // expert's last row tile is often less than half full.  Measured at
-  // T=8192 (256 rows per expert): gate/up 3.78 -> 3.40 ms.  At 64 rows per
-  // expert these tiles measured the same as 64 x 128 on 2 x 2 waves.
+  // expert's last row tile is often less than half full.  Measured on the
+  // hash-routed MXFP4 layer (D=7168, E=256, k=8, I=2048) at T=8192, 256 rows
+  // per expert: gate/up 3.78 -> 3.40 ms.  At 64 rows per expert (T=2048)
+  // these tiles measured the same as 64 x 128 on 2 x 2 waves.
   const bool active = BM < 128 || wm * TBW * 16 < ti.rows;  // uniform per wave
   const uint8_t* X = static_cast<const uint8_t*>(s.A);
 
@@ -174,9 +175,10 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_grouped_gemm_w4a8(GemmAr
   // Scale words of four consecutive stages (stage kt's word in slot kt % 4),
   // loaded together every fourth stage: a row's scales span K / 32 bytes,
   // and reading one 4-byte word of a line per stage let the line leave L2
-  // between stages (measured at recipe 5: gate/up HBM reads 5.91 -> 5.41 GB,
-  // 1.34 -> 1.27 ms).  Loading the weight codes of two stages together (the
-  // two 64-byte halves of a row's line) read 5.13 GB but took 1.38 ms, and
+  // between stages (measured on the hash-routed MXFP4 layer, D=7168, E=256,
+  // k=8, I=2048, at T=2048: gate/up HBM reads 5.91 -> 5.41 GB, 1.34 ->
+  // 1.27 ms).  Loading the weight codes of two stages together (the two
+  // 64-byte halves of a row's line) read 5.13 GB but took 1.38 ms, and
   // 6.13 GB and 1.62 ms with non-temporal loads.
   uint32_t sc[SPT][4];
   auto sload = [&](int kt) {  // kt % 4 == 0; words past the last stage are not loaded
@@ -393,20 +395,22 @@ static int pick_tile_cfg(bool gated, int64_t rows_per_group_hint, bool fp4) {
   if (rows_per_group_hint <= 2) return gated ? TILE_16x16_1x1_P4 : TILE_16x64_1x4_P4;
   if (rows_per_group_hint <= 16) return TILE_32x64_1x4_P4;
   // MXFP4 weights: 128-row tiles on 8 waves, those of the empty row block
-  // loading and staging for the others.  Measured at 64 rows per expert
-  // (recipe-5 gate/up, down): 1.97 and 1.00 ms; 128 x 64 gate/up and
+  // loading and staging for the others.  Measured at 64 rows per expert (the
+  // hash-routed MXFP4 layer, T=2048, D=7168, E=256, k=8, I=2048; gate/up,
+  // down): 1.97 and 1.00 ms; 128 x 64 gate/up and
   // 128 x 128 down on 2 x 2 waves 1.99 and 1.05 ms; 64 x 128 on 1 x 4 waves
   // (each wave decodes and reads all 64 token rows) 2.69 ms; 64 x 64 on 2 x 2
   // waves, where no wave idles, 2.45 ms.
   if (fp4 && rows_per_group_hint <= 96) return gated ? TILE_128x128_2x4_P2 : TILE_128x256_2x4_P2;
   if (rows_per_group_hint <= 96) return gated ? TILE_64x32_4x1_P2 : TILE_64x64_4x1_P2;
   // many rows per expert: gate/up 128 x 128 and down 128 x 256 tiles, both
-  // on 8 waves, two per SIMD (the down GEMM at recipe 3: 1.84 ms, against
+  // on 8 waves, two per SIMD (the down GEMM of the DeepSeek-V3-shaped layer,
+  // T=4096, D=7168, E=256, k=8, I=2048: 1.84 ms, against
   // 1.94 ms for 128 x 128 on 4 waves and 2.23 ms for 128 x 128 on 8; 5.33
   // against 5.64 ms at T=16384).
   // Stages brought into LDS by direct loads (global_load_lds_dwordx4, no
-  // staging registers, a 3- or 4-stage LDS ring) measured no faster at
-  // recipe 3: gate/up 3.35 ms on the 128 x 128 tile with 3 stages, down
+  // staging registers, a 3- or 4-stage LDS ring) measured no faster on
+  // that layer: gate/up 3.35 ms on the 128 x 128 tile with 3 stages, down
   // 2.16 ms on 8 waves with 4; 64-row tiles with a 4-stage ring of mostly
   // weights, 4.22 and 2.20 ms; register-path 64 x 64 (gate/up) and 64 x 128
   // (down) tiles on 2 x 2 waves, three workgroups per CU, 4.48 and 2.27 ms.
